@@ -1,0 +1,239 @@
+/*
+ * libpagedattn — decode-phase paged attention for AMD MI355X (gfx950).
+ *
+ * Each running sequence's single new query attends over its whole KV cache.
+ * The cache lives in fixed-size blocks scattered through one physical pool
+ * and is located through a per-sequence block table: logical block j of a
+ * sequence is physical block table[j], blocks need not be adjacent, and the
+ * attention walks the table block by block (KV 缓存与分页注意力 §06 像内存分页,
+ * §07 块表; Paged Attention in LLMs, "Block Table").
+ *
+ * C ABI.  Every pointer argument is documented as HOST or DEVICE.  The
+ * library never allocates, frees or retains device memory: the caller owns
+ * every buffer (including the optional workspace, whose size is queried
+ * first).  Device work is enqueued on the caller's `stream` (a hipStream_t
+ * passed as void*, NULL = the default stream) and ordered only by it; the
+ * functions return once the work is enqueued.  Argument errors are detected
+ * on the host before anything is enqueued and leave every buffer untouched.
+ * Faults inside kernels surface at the caller's next synchronisation.
+ *
+ * KV pool layout (one pool for K and one for V, per layer), dense row-major:
+ *     pool[num_blocks][num_kv_heads][block_size][head_dim]
+ * so one (block, kv-head) tile is a contiguous block_size x head_dim array.
+ * A token's cache slot is  slot = physical_block * block_size + offset.
+ * q and out are dense [num_seqs][num_heads][head_dim]; new K/V are dense
+ * [num_tokens][num_kv_heads][head_dim].  Query head h reads KV head
+ * h / (num_heads / num_kv_heads) (grouped / multi-query attention, KV 缓存与
+ * 分页注意力 §11 后来的做法).
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PA_F32 = 0,
+    PA_F16 = 1,
+    PA_BF16 = 2,
+    PA_FP8_E4M3 = 3   /* OCP E4M3FN: bias 7, max 448, no inf, NaN = S.1111.111 */
+} pa_dtype;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = -1,   /* bad pointer, size, shape or range            */
+    PA_ERR_UNSUPPORTED = -2,   /* valid but not implemented (dtype pair, head_dim) */
+    PA_ERR_OUT_OF_BLOCKS = -3, /* allocator: not enough free blocks; nothing changed */
+    PA_ERR_INDEX = -4,         /* allocator: logical index / table size out of range */
+    PA_ERR_UNKNOWN_SEQ = -5,   /* allocator: no such sequence id               */
+    PA_ERR_REFCOUNT = -6,      /* allocator: reference count would go negative */
+    PA_ERR_HIP = -7,           /* the HIP runtime refused a launch             */
+    PA_ERR_WORKSPACE = -8,     /* workspace missing or too small               */
+    PA_ERR_EXISTS = -9         /* allocator: sequence id already in use        */
+} pa_status;
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* pa_status_string(int32_t status);
+
+/* Library version string, e.g. "libpagedattn 0.1 gfx950". */
+const char* pa_version(void);
+
+/* Name and description of the HIP error behind the calling thread's last
+ * PA_ERR_HIP (empty string if none).  Valid until the thread's next call. */
+const char* pa_last_error(void);
+
+/*
+ * Per-token KV-cache bytes: 2 x (num_kv_heads x head_dim) x num_layers x
+ * bytes-per-number — one key and one value per layer (KV 缓存与分页注意力
+ * §03 一个词元 800 KB; KV Cache从原理到实战 §2.2 KV Cache的显存账).
+ * Returns -1 for a non-positive size or an unknown dtype.
+ */
+int64_t pa_kv_bytes_per_token(int32_t num_kv_heads, int32_t head_dim, int32_t num_layers,
+                              int32_t dtype);
+
+/*
+ * kv_cache_write — store each new token's K and V once, at its slot.
+ * One token's keys and values are computed once per step and then kept
+ * (KV 缓存与分页注意力 §02 一次写一个词元); the slot comes from the
+ * sequence's block table (§07).
+ *
+ *   k_new, v_new   DEVICE, dense [num_tokens][num_kv_heads][head_dim] of src_dtype
+ *   k_pool, v_pool DEVICE, pool layout above, kv_dtype
+ *   slot_mapping   DEVICE int64 [num_tokens]; slot of token i, -1 = skip.  Slots
+ *                  outside [0, num_blocks*block_size) are skipped as well.  Two
+ *                  tokens with the same slot in one call: undefined which wins.
+ *   Dtype pairs: src == kv (bytes copied unchanged), or kv == PA_FP8_E4M3 with
+ *   src in {F32, F16, BF16}: value x is stored as e4m3(float(x) * (1/scale))
+ *   with 1/scale computed in fp32 on the host, saturating to +-448, rounding
+ *   to nearest even, NaN kept as NaN (KV 缓存与分页注意力 §11: 8-bit floats,
+ *   one byte per number).  k_scale/v_scale are ignored for non-fp8 pools and
+ *   must be finite and > 0 for fp8.
+ *   num_tokens == 0 is a no-op.
+ */
+pa_status pa_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype,
+                            void* k_pool, void* v_pool, int32_t kv_dtype,
+                            const int64_t* slot_mapping, int32_t num_tokens,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, float k_scale, float v_scale, void* stream);
+
+/*
+ * Workspace bytes needed by pa_paged_attention_decode with the same
+ * arguments (0 when partition_size == 0 or every sequence fits one
+ * partition).  Returns 0 for invalid sizes.
+ */
+size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size);
+
+/*
+ * paged_attention_decode — one decode step of attention over a paged cache.
+ * For each sequence s and query head h, with n = context_lens[s] and
+ * g = h / (num_heads / num_kv_heads):
+ *     out[s][h] = sum_t softmax_t(scale * q[s][h] . K_s[t][g]) * V_s[t][g]
+ * over tokens t < n, where K_s[t] is read from
+ * k_pool[block_tables[s][t / block_size]][g][t % block_size] (the new query
+ * dotted with every cached key gives the weights; the weighted sum of the
+ * values is the output: KV Cache从原理到实战 §2.1; fetched block by block
+ * through the table: KV 缓存与分页注意力 §07).  n == 0 gives zeros.
+ *
+ *   out            DEVICE [num_seqs][num_heads][head_dim], dtype = q_dtype
+ *                  (rounded to nearest even from fp32 accumulators)
+ *   q              DEVICE [num_seqs][num_heads][head_dim], q_dtype in {F32, F16, BF16}
+ *   k_pool, v_pool DEVICE, pool layout above, kv_dtype.  Supported pairs:
+ *                  kv == q, or kv == PA_FP8_E4M3 with q in {F32, F16, BF16}.
+ *   block_tables   DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                  ceil(n / block_size) are never read.  An entry outside
+ *                  [0, num_blocks) makes its tokens count as absent (never read).
+ *   context_lens   DEVICE int32 [num_seqs]; values are clamped to
+ *                  [0, min(max_context_len, max_blocks_per_seq * block_size)].
+ *   max_context_len  host-known upper bound of context_lens (sizes the launch).
+ *   scale          softmax scale (1/sqrt(head_dim) for standard attention)
+ *   k_scale, v_scale  fp8 per-tensor scales (value = e4m3 code value * scale);
+ *                  ignored unless kv_dtype == PA_FP8_E4M3.
+ *   partition_size 0: single pass, every (sequence, head) handled whole.
+ *                  > 0: split-context — each sequence is cut into partitions
+ *                  of that many tokens, each partition produces (max, sum,
+ *                  output) partials in `workspace`, and a log-sum-exp
+ *                  reduction kernel merges them.  Results agree with the
+ *                  single pass within rounding.
+ *   workspace      DEVICE, >= pa_paged_attention_workspace_size(...) bytes,
+ *                  256-byte aligned; may be NULL when that size is 0.
+ * Limits: head_dim in {64, 128}; block_size a power of two in [1, 256];
+ * num_heads % num_kv_heads == 0; num_seqs * num_heads * partitions < 2^31.
+ */
+pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
+                                    const void* k_pool, const void* v_pool, int32_t kv_dtype,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t max_context_len,
+                                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    float scale, float k_scale, float v_scale,
+                                    int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/*
+ * copy_blocks — the data half of copy-on-write: for each pair (src, dst),
+ * copy physical block src to dst, bit for bit, in the K and V pool of every
+ * layer.  Before a sequence writes into a block it shares with others, the
+ * block is copied and the write goes into the copy (KV 缓存与分页注意力
+ * §08 共用，写时复制).  Issue it on the same stream before the cache write.
+ *
+ *   k_pools, v_pools  HOST arrays of num_layers DEVICE pool pointers
+ *   pairs             HOST int32 [num_pairs][2] = (src, dst), e.g. as
+ *                     returned by pa_alloc_append_slots.  Every id must lie
+ *                     in [0, num_blocks), destinations must be distinct, and
+ *                     no destination may also be a source in the same call.
+ *   num_pairs == 0 or num_layers == 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                         int32_t kv_dtype, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks,
+                         const int32_t* pairs, int32_t num_pairs, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block allocator: free list, per-block reference counts, block tables
+ * and copy-on-write (KV 缓存与分页注意力 §07 块表, §08 共用，写时复制;
+ * KV Cache从原理到实战 §6.2 加上分页管理).  Host memory only, no GPU calls;
+ * one allocator serves every layer (block ids are shared by all layers).
+ * Not thread-safe: serialise calls on one handle.  Every operation that
+ * fails returns an error and leaves the allocator unchanged.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_allocator pa_allocator;
+
+/* free_order: HOST int32 [num_blocks] permutation of 0..num_blocks-1 giving the
+ * initial free list (blocks are taken from its END), or NULL for 0..n-1. */
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                          pa_allocator** out);
+void pa_alloc_destroy(pa_allocator* a);
+
+/* New sequence holding num_tokens tokens: takes ceil(num_tokens/block_size)
+ * blocks, all or none (PA_ERR_OUT_OF_BLOCKS when short; PA_ERR_EXISTS for a
+ * used id). */
+pa_status pa_alloc_add_seq(pa_allocator* a, int64_t seq_id, int32_t num_tokens);
+
+/* Parallel sample: child_id shares every block of parent_id (counts + 1). */
+pa_status pa_alloc_fork(pa_allocator* a, int64_t parent_id, int64_t child_id);
+
+/* One new token for each of n distinct sequences, in order.  A sequence
+ * whose blocks are all full gets a fresh block; one whose partly filled last
+ * block is still shared gets a copy (its count drops by one) and the pair
+ * (old, new) is appended to cow_pairs_out; the last holder writes in place.
+ *   seq_ids          HOST int64 [n]
+ *   slot_mapping_out HOST int64 [n]: slot of each new token
+ *   cow_pairs_out    HOST int32 [n][2] (at most n pairs), may be NULL only if
+ *                    no copy is needed (else PA_ERR_INVALID_ARG, nothing done)
+ *   num_pairs_out    HOST int32 (pairs written)
+ * All or nothing: if the free list is short, nothing changes. */
+pa_status pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t n,
+                                int64_t* slot_mapping_out, int32_t* cow_pairs_out,
+                                int32_t* num_pairs_out);
+
+/* Finished sequence: every block's count drops by one; blocks reaching zero go
+ * back to the free list in table order. */
+pa_status pa_alloc_free_seq(pa_allocator* a, int64_t seq_id);
+
+/* Block tables HOST int32 [n][max_blocks] (-1 padded) and context lengths HOST
+ * int32 [n] of the given sequences.  PA_ERR_INDEX if a table is longer than
+ * max_blocks.  context_lens_out may be NULL. */
+pa_status pa_alloc_export(const pa_allocator* a, const int64_t* seq_ids, int32_t n,
+                          int32_t* block_tables_out, int32_t max_blocks,
+                          int32_t* context_lens_out);
+
+/* Physical block of logical block `logical_idx` (PA_ERR_INDEX past the table;
+ * KV Cache内存优化技术原理与PagedAttention分页注意力实现, the BlockTable sketch). */
+pa_status pa_alloc_physical_block(const pa_allocator* a, int64_t seq_id, int32_t logical_idx,
+                                  int32_t* block_out);
+
+int32_t pa_alloc_num_free(const pa_allocator* a);                   /* -1 if a is NULL */
+int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block);   /* -1 if out of range */
+int32_t pa_alloc_seq_len(const pa_allocator* a, int64_t seq_id);   /* -1 if unknown */
+int32_t pa_alloc_num_seqs(const pa_allocator* a);                   /* -1 if a is NULL */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

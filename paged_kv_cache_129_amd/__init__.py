@@ -1,0 +1,279 @@
+"""Python binding of libpagedattn — decode-phase paged attention on MI355X.
+
+Argument marshalling only: every step of the path runs in the library's
+gfx950 kernels (device work) or its C++ block allocator (host work).  torch
+supplies device memory and streams.  The names mirror the C ABI declared in
+``include/pagedattn.h`` without the ``pa_`` prefix.
+
+Loading fails loudly (``ImportError``) when the shared library has not been
+built; there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
+
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
+DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
+STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED",
+          -3: "PA_ERR_OUT_OF_BLOCKS", -4: "PA_ERR_INDEX", -5: "PA_ERR_UNKNOWN_SEQ",
+          -6: "PA_ERR_REFCOUNT", -7: "PA_ERR_HIP", -8: "PA_ERR_WORKSPACE", -9: "PA_ERR_EXISTS"}
+
+_c_int32_p = ctypes.POINTER(ctypes.c_int32)
+_c_int64_p = ctypes.POINTER(ctypes.c_int64)
+_vp = ctypes.c_void_p
+
+# (name, restype, argtypes) for every exported function of include/pagedattn.h
+_SIGNATURES = [
+    ("pa_status_string", ctypes.c_char_p, [ctypes.c_int32]),
+    ("pa_version", ctypes.c_char_p, []),
+    ("pa_last_error", ctypes.c_char_p, []),
+    ("pa_kv_bytes_per_token", ctypes.c_int64, [ctypes.c_int32] * 4),
+    ("pa_kv_cache_write", ctypes.c_int32,
+     [_vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+      ctypes.c_float, ctypes.c_float, _vp]),
+    ("pa_paged_attention_workspace_size", ctypes.c_size_t, [ctypes.c_int32] * 5),
+    ("pa_paged_attention_decode", ctypes.c_int32,
+     [_vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+      ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
+    ("pa_copy_blocks", ctypes.c_int32,
+     [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _c_int32_p, ctypes.c_int32, _vp]),
+    ("pa_alloc_create", ctypes.c_int32,
+     [ctypes.c_int32, ctypes.c_int32, _c_int32_p, ctypes.POINTER(_vp)]),
+    ("pa_alloc_destroy", None, [_vp]),
+    ("pa_alloc_add_seq", ctypes.c_int32, [_vp, ctypes.c_int64, ctypes.c_int32]),
+    ("pa_alloc_fork", ctypes.c_int32, [_vp, ctypes.c_int64, ctypes.c_int64]),
+    ("pa_alloc_append_slots", ctypes.c_int32,
+     [_vp, _c_int64_p, ctypes.c_int32, _c_int64_p, _c_int32_p, _c_int32_p]),
+    ("pa_alloc_free_seq", ctypes.c_int32, [_vp, ctypes.c_int64]),
+    ("pa_alloc_export", ctypes.c_int32,
+     [_vp, _c_int64_p, ctypes.c_int32, _c_int32_p, ctypes.c_int32, _c_int32_p]),
+    ("pa_alloc_physical_block", ctypes.c_int32, [_vp, ctypes.c_int64, ctypes.c_int32, _c_int32_p]),
+    ("pa_alloc_num_free", ctypes.c_int32, [_vp]),
+    ("pa_alloc_refcount", ctypes.c_int32, [_vp, ctypes.c_int32]),
+    ("pa_alloc_seq_len", ctypes.c_int32, [_vp, ctypes.c_int64]),
+    ("pa_alloc_num_seqs", ctypes.c_int32, [_vp]),
+]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; "
+                          f"g.build()'` (or python paged_kv_cache_129_amd/build.py)")
+    # torch ships its own HIP runtime (same soname, libamdhip64.so.7).  Import
+    # it first so that this library binds to the runtime torch already loaded:
+    # two HIP runtimes in one process do not share devices or memory.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, res, args in _SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.pa_status_string(status).decode()
+        if status == -7:
+            msg += f": {lib.pa_last_error().decode()}"
+        super().__init__(f"{where}: {STATUS.get(status, status)} ({msg})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise PagedAttnError(status, where)
+
+
+def version() -> str:
+    return lib.pa_version().decode()
+
+
+def kv_bytes_per_token(num_kv_heads: int, head_dim: int, num_layers: int, dtype: str) -> int:
+    return int(lib.pa_kv_bytes_per_token(num_kv_heads, head_dim, num_layers, DTYPE_CODES[dtype]))
+
+
+# ------------------------------------------------------------------ torch plumbing
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
+         torch.uint8: PA_FP8_E4M3}
+    fp8 = getattr(torch, "float8_e4m3fn", None)
+    if fp8 is not None:
+        m[fp8] = PA_FP8_E4M3
+    if t.dtype not in m:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev(t, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+# ------------------------------------------------------------------ device calls
+def kv_cache_write(k_new, v_new, k_pool, v_pool, slot_mapping, *, k_scale: float = 1.0,
+                   v_scale: float = 1.0, stream=None) -> None:
+    """Store new tokens' K/V ([T, Hkv, D]) at their slots of [NB, Hkv, bs, D] pools."""
+    T, Hkv, D = k_new.shape
+    NB, Hkv2, bs, D2 = k_pool.shape
+    if (Hkv, D) != (Hkv2, D2) or v_new.shape != k_new.shape or v_pool.shape != k_pool.shape:
+        raise ValueError("shape mismatch")
+    if slot_mapping.dtype != _torch().int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    _check(lib.pa_kv_cache_write(_dev(k_new, "k_new"), _dev(v_new, "v_new"), dtype_code(k_new),
+                                 _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
+                                 dtype_code(k_pool), _dev(slot_mapping, "slot_mapping"), T, Hkv, D,
+                                 bs, NB, k_scale, v_scale, _stream(stream, k_pool.device)),
+           "kv_cache_write")
+
+
+def paged_attention_workspace_size(num_seqs: int, num_heads: int, head_dim: int,
+                                   max_context_len: int, partition_size: int) -> int:
+    return int(lib.pa_paged_attention_workspace_size(num_seqs, num_heads, head_dim,
+                                                     max_context_len, partition_size))
+
+
+def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, *,
+                           max_context_len: int, scale: float, k_scale: float = 1.0,
+                           v_scale: float = 1.0, partition_size: int = 0, workspace=None,
+                           stream=None) -> None:
+    """out[S, H, D] = decode attention of q[S, H, D] over paged [NB, Hkv, bs, D] pools."""
+    torch = _torch()
+    S, H, D = q.shape
+    NB, Hkv, bs, D2 = k_pool.shape
+    if D2 != D or out.shape != q.shape or out.dtype != q.dtype or v_pool.shape != k_pool.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [S, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
+        raise ValueError("context_lens must be int32 [S]")
+    need = paged_attention_workspace_size(S, H, D, max_context_len, partition_size)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_paged_attention_decode(
+        _dev(out, "out"), _dev(q, "q"), dtype_code(q), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"), dtype_code(k_pool), _dev(block_tables, "block_tables"),
+        block_tables.shape[1], _dev(context_lens, "context_lens"), int(max_context_len), S, H,
+        Hkv, D, bs, NB, float(scale), float(k_scale), float(v_scale), int(partition_size),
+        ws_ptr, ws_bytes, _stream(stream, q.device)), "paged_attention_decode")
+
+
+def copy_blocks(k_pools: Sequence, v_pools: Sequence, pairs, *, stream=None) -> None:
+    """Copy block src -> dst for every (src, dst) in ``pairs`` in every layer's K and V pool."""
+    pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    L = len(k_pools)
+    if L != len(v_pools):
+        raise ValueError("k_pools and v_pools differ in length")
+    if L == 0 or len(pairs) == 0:
+        return
+    NB, Hkv, bs, D = k_pools[0].shape
+    for p in list(k_pools) + list(v_pools):
+        if p.shape != k_pools[0].shape or p.dtype != k_pools[0].dtype:
+            raise ValueError("all pools must share shape and dtype")
+    kp = (ctypes.c_void_p * L)(*[_dev(p, "k_pool").value for p in k_pools])
+    vp = (ctypes.c_void_p * L)(*[_dev(p, "v_pool").value for p in v_pools])
+    _check(lib.pa_copy_blocks(kp, vp, L, dtype_code(k_pools[0]), Hkv, D, bs, NB,
+                              pairs.ctypes.data_as(_c_int32_p), len(pairs),
+                              _stream(stream, k_pools[0].device)), "copy_blocks")
+
+
+# ------------------------------------------------------------------ host allocator
+class BlockAllocator:
+    """Host block allocator (free list, reference counts, copy-on-write) in C++."""
+
+    def __init__(self, num_blocks: int, block_size: int, free_order: Optional[Sequence[int]] = None):
+        self._h = ctypes.c_void_p()
+        fo = None
+        if free_order is not None:
+            self._fo = np.ascontiguousarray(np.asarray(free_order, dtype=np.int32))
+            fo = self._fo.ctypes.data_as(_c_int32_p)
+        _check(lib.pa_alloc_create(num_blocks, block_size, fo, ctypes.byref(self._h)),
+               "alloc_create")
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            lib.pa_alloc_destroy(h)
+            self._h = None
+
+    def add_seq(self, seq_id: int, num_tokens: int) -> None:
+        _check(lib.pa_alloc_add_seq(self._h, seq_id, num_tokens), "alloc_add_seq")
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        _check(lib.pa_alloc_fork(self._h, parent_id, child_id), "alloc_fork")
+
+    def append_slots(self, seq_ids: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        n = len(ids)
+        slots = np.empty(n, dtype=np.int64)
+        pairs = np.empty((max(n, 1), 2), dtype=np.int32)
+        npairs = ctypes.c_int32(0)
+        _check(lib.pa_alloc_append_slots(self._h, ids.ctypes.data_as(_c_int64_p), n,
+                                         slots.ctypes.data_as(_c_int64_p),
+                                         pairs.ctypes.data_as(_c_int32_p), ctypes.byref(npairs)),
+               "alloc_append_slots")
+        return slots, pairs[:npairs.value].copy()
+
+    def free_seq(self, seq_id: int) -> None:
+        _check(lib.pa_alloc_free_seq(self._h, seq_id), "alloc_free_seq")
+
+    def export(self, seq_ids: Sequence[int], max_blocks: int) -> Tuple[np.ndarray, np.ndarray]:
+        ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
+        tables = np.empty((len(ids), max_blocks), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        _check(lib.pa_alloc_export(self._h, ids.ctypes.data_as(_c_int64_p), len(ids),
+                                   tables.ctypes.data_as(_c_int32_p), max_blocks,
+                                   lens.ctypes.data_as(_c_int32_p)), "alloc_export")
+        return tables, lens
+
+    def physical_block(self, seq_id: int, logical_idx: int) -> int:
+        out = ctypes.c_int32(0)
+        _check(lib.pa_alloc_physical_block(self._h, seq_id, logical_idx, ctypes.byref(out)),
+               "alloc_physical_block")
+        return out.value
+
+    def num_free(self) -> int:
+        return int(lib.pa_alloc_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(lib.pa_alloc_refcount(self._h, block))
+
+    def seq_len(self, seq_id: int) -> int:
+        return int(lib.pa_alloc_seq_len(self._h, seq_id))
+
+    def num_seqs(self) -> int:
+        return int(lib.pa_alloc_num_seqs(self._h))

@@ -1,0 +1,244 @@
+// C-ABI entry points: argument validation (host, before anything is
+// enqueued), then dispatch to the gfx950 kernels on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <unordered_set>
+
+#include "kernels.h"
+#include "pa_device.h"
+#include "pagedattn.h"
+
+namespace {
+
+bool valid_dtype(int32_t dt) { return dt >= PA_F32 && dt <= PA_FP8_E4M3; }
+
+int log2_exact(int32_t v) {
+    if (v <= 0 || (v & (v - 1))) return -1;
+    int l = 0;
+    while ((1 << l) < v) ++l;
+    return l;
+}
+
+bool supported_head_dim(int32_t d) { return d == 64 || d == 128; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+thread_local char g_last_error[256] = "";
+
+// Launch through `fn` after clearing any error an earlier, unrelated runtime
+// call left behind, so that only this launch's own failure is reported.
+template <typename F>
+pa_status launch_checked(F&& fn) {
+    (void)hipGetLastError();
+    g_last_error[0] = 0;
+    const hipError_t e = fn();
+    if (e == hipSuccess) return PA_OK;
+    snprintf(g_last_error, sizeof(g_last_error), "%s: %s", hipGetErrorName(e), hipGetErrorString(e));
+    return PA_ERR_HIP;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int64_t num_partitions(int32_t ctx_cap, int32_t partition_size) {
+    if (partition_size <= 0 || ctx_cap <= 0) return 1;
+    return ((int64_t)ctx_cap + partition_size - 1) / partition_size;
+}
+
+size_t partial_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_dim, int64_t parts) {
+    if (parts <= 1) return 0;
+    const size_t b = (size_t)num_seqs * num_heads * parts * (size_t)(head_dim + 2) * sizeof(float);
+    return (b + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int32_t status) {
+    switch (status) {
+        case PA_OK: return "ok";
+        case PA_ERR_INVALID_ARG: return "invalid argument";
+        case PA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PA_ERR_OUT_OF_BLOCKS: return "Out of KV cache blocks";
+        case PA_ERR_INDEX: return "index out of range";
+        case PA_ERR_UNKNOWN_SEQ: return "unknown sequence id";
+        case PA_ERR_REFCOUNT: return "reference count error";
+        case PA_ERR_HIP: return "HIP runtime error";
+        case PA_ERR_WORKSPACE: return "workspace missing or too small";
+        case PA_ERR_EXISTS: return "sequence id already exists";
+        default: return "unknown status";
+    }
+}
+
+const char* pa_version(void) { return "libpagedattn 0.1 gfx950"; }
+
+const char* pa_last_error(void) { return g_last_error; }
+
+int64_t pa_kv_bytes_per_token(int32_t num_kv_heads, int32_t head_dim, int32_t num_layers,
+                              int32_t dtype) {
+    if (num_kv_heads <= 0 || head_dim <= 0 || num_layers <= 0 || !valid_dtype(dtype)) return -1;
+    return 2 * (int64_t)num_kv_heads * head_dim * num_layers * pa::elem_bytes(dtype);
+}
+
+pa_status pa_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype,
+                            void* k_pool, void* v_pool, int32_t kv_dtype,
+                            const int64_t* slot_mapping, int32_t num_tokens,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, float k_scale, float v_scale, void* stream) {
+    if (!valid_dtype(src_dtype) || !valid_dtype(kv_dtype)) return PA_ERR_INVALID_ARG;
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
+        return PA_ERR_INVALID_ARG;
+    const int lbs = log2_exact(block_size);
+    if (lbs < 0 || lbs > 8) return PA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+    const bool quantise = kv_dtype == PA_FP8_E4M3 && src_dtype != PA_FP8_E4M3;
+    if (src_dtype != kv_dtype && !quantise) return PA_ERR_UNSUPPORTED;
+    if (quantise && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
+                      v_scale > 0.0f))
+        return PA_ERR_INVALID_ARG;
+    if (num_tokens == 0) return PA_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping) return PA_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_INVALID_ARG;
+    pa::WriteArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.log2_bs = lbs;
+    a.num_slots = (int64_t)num_blocks * block_size;
+    a.k_inv_scale = quantise ? 1.0f / k_scale : 1.0f;     // IEEE fp32 division
+    a.v_inv_scale = quantise ? 1.0f / v_scale : 1.0f;
+    return launch_checked([&] { return pa::launch_kv_write(a, src_dtype, kv_dtype, as_stream(stream)); });
+}
+
+size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                         int32_t max_context_len, int32_t partition_size) {
+    if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
+        partition_size < 0)
+        return 0;
+    return partial_bytes(num_seqs, num_heads, head_dim,
+                         num_partitions(max_context_len, partition_size));
+}
+
+pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
+                                    const void* k_pool, const void* v_pool, int32_t kv_dtype,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t max_context_len,
+                                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    float scale, float k_scale, float v_scale,
+                                    int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype)) return PA_ERR_INVALID_ARG;
+    if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0)
+        return PA_ERR_INVALID_ARG;
+    if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    const int lbs = log2_exact(block_size);
+    if (lbs < 0 || lbs > 8) return PA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+    if (q_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+    if (kv_dtype != q_dtype && kv_dtype != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+    if (kv_dtype == PA_FP8_E4M3 && !(std::isfinite(k_scale) && k_scale > 0.0f &&
+                                     std::isfinite(v_scale) && v_scale > 0.0f))
+        return PA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0) return PA_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_INVALID_ARG;
+
+    const int64_t cap64 = std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq << lbs);
+    const int32_t ctx_cap = (int32_t)std::min<int64_t>(cap64, INT32_MAX);
+    const int64_t parts = num_partitions(ctx_cap, partition_size);
+    if ((int64_t)num_seqs * num_heads * parts >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
+    const size_t need = partial_bytes(num_seqs, num_heads, head_dim, parts);
+    if (need > 0 && (!workspace || workspace_bytes < need ||
+                     (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+        return PA_ERR_WORKSPACE;
+
+    pa::DecodeArgs a{};
+    a.q = q;
+    a.out = out;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.tables = block_tables;
+    a.ctx_lens = context_lens;
+    a.ws = reinterpret_cast<float*>(workspace);
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks = max_blocks_per_seq;
+    a.ctx_cap = ctx_cap;
+    a.num_blocks = num_blocks;
+    a.log2_bs = lbs;
+    a.num_parts = (int32_t)parts;
+    a.part_tokens = parts > 1 ? partition_size : std::max<int32_t>(ctx_cap, 1);
+    const float kfac = kv_dtype == PA_FP8_E4M3 ? k_scale * pa::dequant_factor(kv_dtype) : 1.0f;
+    const float vfac = kv_dtype == PA_FP8_E4M3 ? v_scale * pa::dequant_factor(kv_dtype) : 1.0f;
+    a.qk_scale = scale * pa::kLog2e * kfac;
+    a.out_scale = vfac;
+    return launch_checked(
+        [&] { return pa::launch_decode(a, q_dtype, kv_dtype, head_dim, as_stream(stream)); });
+}
+
+pa_status pa_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
+                         int32_t kv_dtype, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, const int32_t* pairs,
+                         int32_t num_pairs, void* stream) {
+    if (!valid_dtype(kv_dtype) || num_layers < 0 || num_pairs < 0 || num_kv_heads <= 0 ||
+        head_dim <= 0 || num_blocks <= 0)
+        return PA_ERR_INVALID_ARG;
+    const int lbs = log2_exact(block_size);
+    if (lbs < 0 || lbs > 8) return PA_ERR_INVALID_ARG;
+    const int64_t block_bytes =
+        (int64_t)num_kv_heads * block_size * head_dim * pa::elem_bytes(kv_dtype);
+    if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+    if (num_layers == 0 || num_pairs == 0) return PA_OK;
+    if (!k_pools || !v_pools || !pairs) return PA_ERR_INVALID_ARG;
+    for (int32_t l = 0; l < num_layers; ++l)
+        if (!k_pools[l] || !v_pools[l] || !aligned16(k_pools[l]) || !aligned16(v_pools[l]))
+            return PA_ERR_INVALID_ARG;
+    std::unordered_set<int32_t> dsts, srcs;
+    for (int32_t i = 0; i < num_pairs; ++i) {
+        const int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
+        if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks || s == d) return PA_ERR_INVALID_ARG;
+        if (!dsts.insert(d).second) return PA_ERR_INVALID_ARG;
+        srcs.insert(s);
+    }
+    for (int32_t d : dsts)
+        if (srcs.count(d)) return PA_ERR_INVALID_ARG;
+
+    for (int32_t l0 = 0; l0 < num_layers; l0 += pa::kCopyMaxLayers) {
+        for (int32_t p0 = 0; p0 < num_pairs; p0 += pa::kCopyMaxPairs) {
+            pa::CopyArgs a{};
+            a.block_bytes = block_bytes;
+            a.num_layers = std::min(num_layers - l0, pa::kCopyMaxLayers);
+            a.num_pairs = std::min(num_pairs - p0, pa::kCopyMaxPairs);
+            for (int32_t l = 0; l < a.num_layers; ++l) {
+                a.k[l] = k_pools[l0 + l];
+                a.v[l] = v_pools[l0 + l];
+            }
+            for (int32_t i = 0; i < a.num_pairs; ++i) {
+                a.src[i] = pairs[2 * (p0 + i)];
+                a.dst[i] = pairs[2 * (p0 + i) + 1];
+            }
+            const pa_status st =
+                launch_checked([&] { return pa::launch_copy_blocks(a, as_stream(stream)); });
+            if (st != PA_OK) return st;
+        }
+    }
+    return PA_OK;
+}
+
+}  // extern "C"

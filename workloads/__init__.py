@@ -315,3 +315,116 @@ def token_values(config: str, tensor: str, stream: int, n: int, num_kv_heads: in
     """fp32 N(0,1) values for ``n`` tokens of stream ``stream`` (a sequence or a prompt)."""
     r = rng_for(config, layer, tensor, salt=stream)
     return r.standard_normal((n, num_kv_heads, head_dim), dtype=np.float32) * np.float32(value_scale)
+
+
+def shared_prompt_case(alloc, spec: SharedPromptSpec, *, num_heads: int = 64, num_kv_heads: int = 8,
+                       head_dim: int = 128, block_size: int = 16, num_blocks: int = 12288,
+                       kv_dtype: str = "bf16", q_dtype: str = "bf16", config: str = "llama70b",
+                       layer: int = 0):
+    """Parallel-sampling batch laid out by ``alloc`` (any object with add_seq / fork /
+    append_slots / export, e.g. the library allocator or the oracle's model).
+
+    Independent sequences get their own blocks; each group's ``samples``
+    sequences fork one prompt and so share its blocks.  The pool holds the
+    pre-append tokens (values drawn per sequence / per prompt); the returned
+    case carries the post-append tables and lengths, the slots of the new
+    tokens, and the copy-on-write pairs the allocator emitted, which must be
+    applied before the write.
+    """
+    ctx_pre = np.asarray(spec.independent_ctx, dtype=np.int64)
+    n_ind = len(ctx_pre)
+    S = n_ind + spec.groups * spec.samples
+    H, Hkv, D, bs = num_heads, num_kv_heads, head_dim, block_size
+    for i, n in enumerate(ctx_pre):
+        alloc.add_seq(i, int(n))
+    for g in range(spec.groups):
+        parent = n_ind + g * spec.samples
+        alloc.add_seq(parent, spec.prompt_len)
+        for j in range(1, spec.samples):
+            alloc.fork(parent, parent + j)
+    ids = list(range(S))
+    pre_lens = np.concatenate([ctx_pre, np.full(spec.groups * spec.samples, spec.prompt_len)])
+    max_blocks = int((int(pre_lens.max()) + 1 + bs - 1) // bs) + 1
+    tables_pre, lens_pre = alloc.export(ids, max_blocks)
+    k_pool = empty_pool(num_blocks, Hkv, bs, D, kv_dtype)
+    v_pool = empty_pool(num_blocks, Hkv, bs, D, kv_dtype)
+    for i in range(n_ind):
+        n = int(ctx_pre[i])
+        fill_tokens(k_pool, tables_pre[i], to_storage(token_values(config, "k", i, n, Hkv, D,
+                                                                   layer=layer), kv_dtype), bs)
+        fill_tokens(v_pool, tables_pre[i], to_storage(token_values(config, "v", i, n, Hkv, D,
+                                                                   layer=layer), kv_dtype), bs)
+    for g in range(spec.groups):
+        parent = n_ind + g * spec.samples
+        P = spec.prompt_len
+        fill_tokens(k_pool, tables_pre[parent], to_storage(
+            token_values(config, "prompt_k", g, P, Hkv, D, layer=layer), kv_dtype), bs)
+        fill_tokens(v_pool, tables_pre[parent], to_storage(
+            token_values(config, "prompt_v", g, P, Hkv, D, layer=layer), kv_dtype), bs)
+    slots, pairs = alloc.append_slots(ids)
+    tables, lens = alloc.export(ids, max_blocks)
+    r = rng_for(config, layer, "misc")
+    k_new = to_storage(r.standard_normal((S, Hkv, D), dtype=np.float32), q_dtype)
+    v_new = to_storage(r.standard_normal((S, Hkv, D), dtype=np.float32), q_dtype)
+    q = to_storage(r.standard_normal((S, H, D), dtype=np.float32), q_dtype)
+    case = DecodeCase(name=f"{config}_shared", num_seqs=S, num_heads=H, num_kv_heads=Hkv,
+                      head_dim=D, block_size=bs, num_blocks=num_blocks, kv_dtype=kv_dtype,
+                      q_dtype=q_dtype, context_lens=np.asarray(lens, dtype=np.int32),
+                      block_tables=np.asarray(tables, dtype=np.int32), k_pool=k_pool,
+                      v_pool=v_pool, k_new=k_new, v_new=v_new,
+                      slot_mapping=np.asarray(slots, dtype=np.int64), q=q,
+                      scale=1.0 / math.sqrt(D))
+    return case, np.asarray(pairs, dtype=np.int32).reshape(-1, 2)
+
+
+def free_order(config: str, num_blocks: int) -> np.ndarray:
+    """Seeded shuffle of the pool used as an allocator's initial free list."""
+    return rng_for(config, 0, "free").permutation(num_blocks).astype(np.int32)
+
+
+def device_pool_case(name: str, config: str, *, num_seqs: int, num_heads: int, num_kv_heads: int,
+                     head_dim: int, block_size: int, context_lens: Sequence[int], kv_dtype: str,
+                     num_blocks: int, layer: int = 0, device: str = "cuda", seed: int = 0,
+                     max_blocks: Optional[int] = None, place_layer: Optional[int] = None):
+    """Large decode case generated on the device with torch's seeded generator.
+
+    Returns a dict of device tensors (pre-append pools with NaN poison in
+    every slot that holds no live token, new tokens, query, tables, lengths,
+    slots).  Used where host generation would be too slow (4 GiB pools).
+    """
+    import torch
+    ctx = np.asarray(context_lens, dtype=np.int32)
+    S, H, Hkv, D, bs = num_seqs, num_heads, num_kv_heads, head_dim, block_size
+    tdt = {"f16": torch.float16, "bf16": torch.bfloat16, "f32": torch.float32}[kv_dtype]
+    nbs = blocks_needed(ctx, bs)
+    # one block table per sequence serves every layer: placement may come from another layer
+    tables = place_blocks(rng_for(config, layer if place_layer is None else place_layer, "place"),
+                          num_blocks, nbs, max_blocks)
+    g = torch.Generator(device=device)
+    g.manual_seed(1_000_003 * (layer + 1) + 7919 * seed + _CONFIG_IDS.get(config, 99))
+    shape = (num_blocks, Hkv, bs, D)
+    k_pool = torch.empty(shape, dtype=tdt, device=device)
+    v_pool = torch.empty(shape, dtype=tdt, device=device)
+    for p in (k_pool, v_pool):
+        for b0 in range(0, num_blocks, 4096):          # bounded temporaries
+            b1 = min(num_blocks, b0 + 4096)
+            p[b0:b1].normal_(generator=g)
+    nan = float("nan")
+    used = np.zeros(num_blocks, dtype=bool)
+    for s in range(S):
+        used[tables[s, :nbs[s]]] = True
+    free = torch.from_numpy(np.nonzero(~used)[0]).to(device)
+    for p in (k_pool, v_pool):
+        if free.numel():
+            p[free] = nan
+        for s in range(S):
+            n = int(ctx[s])
+            for t in range(max(n - 1, 0), int(nbs[s]) * bs):       # new token's slot and the tail
+                p[int(tables[s, t // bs]), :, t % bs, :] = nan
+    k_new = torch.randn((S, Hkv, D), generator=g, device=device, dtype=torch.float32).to(tdt)
+    v_new = torch.randn((S, Hkv, D), generator=g, device=device, dtype=torch.float32).to(tdt)
+    q = torch.randn((S, H, D), generator=g, device=device, dtype=torch.float32).to(tdt)
+    slots = slots_of(tables, ctx.astype(np.int64) - 1, bs)
+    return dict(name=name, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new, q=q,
+                tables=tables, ctx=ctx, slots=slots, num_heads=H, num_kv_heads=Hkv, head_dim=D,
+                block_size=bs, num_blocks=num_blocks, kv_dtype=kv_dtype, scale=1.0 / math.sqrt(D))
