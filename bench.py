@@ -50,17 +50,122 @@ def write_bytes(num_tokens, num_kv_heads, head_dim, src_bytes, kv_bytes):
 
 
 # ---------------------------------------------------------------- workloads
-class Llama7B:
+class Workload:
+    """A decode step over ``L`` layers, each with its own pools in HBM.
+
+    Subclasses fill: S, H, Hkv, D, bs, L, ctx, kv_dtype, q_dtype, layers (list of
+    dicts of device tensors: k_pool, v_pool, k_new, v_new, q, out), tables,
+    ctx_t, slots, scale, k_scale, v_scale, attn_bytes, write_bytes.
+    """
+    pairs = None            # copy-on-write pairs applied each step (shared-prompt batch)
+    k_scale = v_scale = 1.0
+
+    def finish(self, pa, torch, partition_size, max_ctx):
+        self.pa, self.torch = pa, torch
+        self.partition_size = partition_size
+        self.max_ctx = int(max_ctx)
+        ws = pa.paged_attention_workspace_size(self.S, self.H, self.D, self.max_ctx, partition_size)
+        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda")
+        for d in self.layers:
+            d.setdefault("out", torch.empty_like(d["q"]))
+        self.step_bytes = self.L * (self.attn_bytes + self.write_bytes) + \
+            (0 if self.pairs is None else self.L * len(self.pairs) * 2 * 2 * self.block_bytes)
+        self.seq_layers_per_step = self.S * self.L
+
+    def decode(self, l):
+        d = self.layers[l]
+        self.pa.paged_attention_decode(d["out"], d["q"], d["k_pool"], d["v_pool"], self.tables,
+                                       self.ctx_t, max_context_len=self.max_ctx, scale=self.scale,
+                                       k_scale=self.k_scale, v_scale=self.v_scale,
+                                       partition_size=self.partition_size, workspace=self.ws)
+
+    def step(self):
+        if self.pairs is not None and len(self.pairs):
+            self.pa.copy_blocks([d["k_pool"] for d in self.layers],
+                                [d["v_pool"] for d in self.layers], self.pairs)
+        for l in range(self.L):
+            d = self.layers[l]
+            self.pa.kv_cache_write(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], self.slots,
+                                   k_scale=self.k_scale, v_scale=self.v_scale)
+            self.decode(l)
+
+    def config(self):
+        return {"workload": self.name, "num_seqs": self.S, "num_layers": self.L,
+                "num_heads": self.H, "num_kv_heads": self.Hkv, "head_dim": self.D,
+                "block_size": self.bs, "kv_dtype": self.kv_dtype, "q_dtype": self.q_dtype,
+                "context_lens": self.ctx_desc, "partition_size": self.partition_size}
+
+    def cpu_sample(self, oracle, budget_s):
+        """Oracle write + attention, one sequence (all heads) of layer 0 at a time."""
+        torch = self.torch
+        d = self.layers[0]
+        tables = self.tables.cpu().numpy()
+        ctx = self.ctx
+        done, secs, bytes_done = 0, 0.0, 0
+        kn_all, vn_all = d["k_new"].cpu(), d["v_new"].cpu()
+        q_all = d["q"].cpu()
+        slots = self.slots.cpu().numpy()
+        order = np.argsort(-ctx, kind="stable")          # longest first: the work that matters
+        for s in order:
+            if secs >= budget_s:
+                break
+            n = int(ctx[s])
+            nblk = (n + self.bs - 1) // self.bs
+            idx = torch.from_numpy(tables[s, :nblk].astype(np.int64)).cuda()
+            kp, vp = raw_np(d["k_pool"][idx]), raw_np(d["v_pool"][idx])
+            local = np.arange(nblk, dtype=np.int32)[None, :]
+            pos = n - 1
+            slot = np.array([(pos // self.bs) * self.bs + pos % self.bs])
+            kn, vn = raw_np(kn_all[s:s + 1]), raw_np(vn_all[s:s + 1])
+            q = raw_np(q_all[s:s + 1])
+            t0 = time.perf_counter()
+            oracle.kv_write(kp, vp, self.kv_dtype, kn, vn, self.q_dtype, slot, self.bs,
+                            self.k_scale, self.v_scale)
+            oracle.paged_attention(q, self.q_dtype, kp, vp, self.kv_dtype, local, [n], self.bs,
+                                   self.scale, self.k_scale, self.v_scale)
+            secs += time.perf_counter() - t0
+            done += 1
+            bytes_done += n * 2 * self.Hkv * self.D * ELEM[self.kv_dtype]
+        sample = (f"{done} sequence-layers of layer 0 (one sequence, all {self.H} heads, "
+                  f"longest contexts first, {bytes_done / 1e6:.1f} MB of K/V)")
+        return done, secs, bytes_done, sample
+
+
+ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
+
+
+def raw_np(t):
+    """Device tensor -> numpy storage array (bf16 as raw uint16)."""
+    t = t.detach().cpu()
+    if t.dtype.__str__() == "torch.bfloat16":
+        import torch
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def upload_case(case, torch):
+    import workloads as W
+    def dev(a, dt):
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dt == "bf16":
+            t = t.view(torch.int16).view(torch.bfloat16)
+        return t.cuda()
+    return {"k_pool": dev(case.k_pool, case.kv_dtype), "v_pool": dev(case.v_pool, case.kv_dtype),
+            "k_new": dev(case.k_new, case.q_dtype), "v_new": dev(case.v_new, case.q_dtype),
+            "q": dev(case.q, case.q_dtype)}
+
+
+class Llama7B(Workload):
     """Llama-2-7B-shaped decode step over all 32 layers: 64 sequences at context
     4096, 32 heads x 128, block size 16, fp16 cache, 17,408-block pool per layer
     (4.25 GiB of K+V per layer, 136 GiB in all), one block table for all layers."""
     name = "llama2-7b decode step, 32 layers, fp16 KV"
 
-    def __init__(self, pa, W, torch, partition_size):
-        self.pa, self.torch = pa, torch
+    def __init__(self, pa, W, torch, partition_size, args):
         self.S, self.H, self.Hkv, self.D, self.bs, self.NB, self.L = 64, 32, 32, 128, 16, 17408, 32
+        self.kv_dtype = self.q_dtype = "f16"
         self.ctx = np.full(self.S, 4096, dtype=np.int32)
-        self.partition_size = partition_size
+        self.ctx_desc = "all 4096"
         self.layers = []
         t0 = time.time()
         for l in range(self.L):
@@ -68,7 +173,6 @@ class Llama7B:
                                    num_kv_heads=self.Hkv, head_dim=self.D, block_size=self.bs,
                                    context_lens=self.ctx, kv_dtype="f16", num_blocks=self.NB,
                                    layer=l, place_layer=0)
-            d["out"] = torch.empty_like(d["q"])
             self.layers.append(d)
         torch.cuda.synchronize()
         log(f"generated {self.L} layers of pools in {time.time() - t0:.1f}s")
@@ -76,59 +180,149 @@ class Llama7B:
         self.tables = torch.from_numpy(d0["tables"]).cuda()
         self.ctx_t = torch.from_numpy(self.ctx).cuda()
         self.slots = torch.from_numpy(d0["slots"]).cuda()
-        ws = pa.paged_attention_workspace_size(self.S, self.H, self.D, 4096, partition_size)
-        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda")
         self.scale = d0["scale"]
         self.attn_bytes = attention_bytes(self.ctx, self.S, self.H, self.Hkv, self.D, 2, 2, self.bs)
         self.write_bytes = write_bytes(self.S, self.Hkv, self.D, 2, 2)
-        self.step_bytes = self.L * (self.attn_bytes + self.write_bytes)
-        self.seq_layers_per_step = self.S * self.L
-
-    def decode(self, l):
-        d = self.layers[l]
-        self.pa.paged_attention_decode(d["out"], d["q"], d["k_pool"], d["v_pool"], self.tables,
-                                       self.ctx_t, max_context_len=4096, scale=self.scale,
-                                       partition_size=self.partition_size, workspace=self.ws)
-
-    def step(self):
-        for l in range(self.L):
-            d = self.layers[l]
-            self.pa.kv_cache_write(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], self.slots)
-            self.decode(l)
-
-    def num_decode_units(self):
-        return self.L
+        self.finish(pa, torch, partition_size, 4096)
 
     def config(self):
-        return {"workload": self.name, "num_seqs": self.S, "context_len": 4096, "num_layers": self.L,
-                "num_heads": self.H, "num_kv_heads": self.Hkv, "head_dim": self.D,
-                "block_size": self.bs, "num_blocks_per_layer": self.NB, "kv_dtype": "f16",
-                "partition_size": self.partition_size}
-
-    def cpu_sample(self, oracle, budget_s):
-        """Oracle write + attention for single sequences of layer 0 (all 32 heads)."""
-        torch = self.torch
-        d = self.layers[0]
-        nblk = 4096 // self.bs
-        done, t_total = 0, 0.0
-        s = 0
-        while t_total < budget_s and s < self.S:
-            idx = torch.from_numpy(d["tables"][s, :nblk]).long().cuda()
-            kp, vp = d["k_pool"][idx].cpu().numpy(), d["v_pool"][idx].cpu().numpy()
-            q = d["q"][s:s + 1].cpu().numpy()
-            kn, vn = d["k_new"][s:s + 1].cpu().numpy(), d["v_new"][s:s + 1].cpu().numpy()
-            table = np.arange(nblk, dtype=np.int32)[None, :]
-            slot = np.array([(nblk - 1) * self.bs + self.bs - 1])
-            t0 = time.perf_counter()
-            oracle.kv_write(kp, vp, "f16", kn, vn, "f16", slot, self.bs)
-            oracle.paged_attention(q, "f16", kp, vp, "f16", table, [4096], self.bs, self.scale)
-            t_total += time.perf_counter() - t0
-            done += 1
-            s += 1
-        return done, t_total, f"{done} sequence-layers (one sequence, all 32 heads, context 4096, layer 0)"
+        c = super().config()
+        c["num_blocks_per_layer"] = self.NB
+        return c
 
 
-WORKLOADS = {"llama7b": Llama7B}
+class HostLayers(Workload):
+    """Workloads small enough to generate on the host: layer 0 comes from the
+    seeded generator, the other layers are copies of it in their own memory
+    (distinct addresses, so no layer's K/V can be served from another's cache
+    lines; the 256 MB last-level cache cannot hold the step's working set)."""
+
+    def place(self, torch, case, L):
+        self.case = case
+        self.S, self.H, self.Hkv, self.D = case.num_seqs, case.num_heads, case.num_kv_heads, case.head_dim
+        self.bs, self.NB, self.L = case.block_size, case.num_blocks, L
+        self.kv_dtype, self.q_dtype = case.kv_dtype, case.q_dtype
+        self.ctx = case.context_lens.astype(np.int32)
+        self.scale, self.k_scale, self.v_scale = case.scale, case.k_scale, case.v_scale
+        base = upload_case(case, torch)
+        self.layers = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(L - 1)]
+        self.tables = torch.from_numpy(case.block_tables.astype(np.int32)).cuda()
+        self.ctx_t = torch.from_numpy(self.ctx).cuda()
+        self.slots = torch.from_numpy(case.slot_mapping.astype(np.int64)).cuda()
+        self.block_bytes = self.Hkv * self.bs * self.D * ELEM[self.kv_dtype]
+        self.write_bytes = write_bytes(self.S, self.Hkv, self.D, ELEM[self.q_dtype], ELEM[self.kv_dtype])
+        torch.cuda.synchronize()
+
+
+class Opt13B(HostLayers):
+    """OPT-13B-shaped layer (40 heads x 128, fp16, block 16, 30 sequences with
+    log-normal contexts, 1,000-block pool), stepped over OPT-13B's 40 layers."""
+    name = "opt-13b decode step, 40 layers, fp16 KV"
+
+    def __init__(self, pa, W, torch, partition_size, args):
+        case = W.opt13b_case()
+        self.place(torch, case, 40)
+        self.ctx_desc = f"log-normal median 300, sum {int(self.ctx.sum())}, max {int(self.ctx.max())}"
+        self.attn_bytes = attention_bytes(self.ctx, self.S, self.H, self.Hkv, self.D, 2, 2, self.bs)
+        self.finish(pa, torch, partition_size, self.ctx.max())
+
+
+class Falcon7B(HostLayers):
+    """Falcon-7B-shaped MQA layer: 71 query heads share 1 KV head of 64, fp8 e4m3
+    cache with per-tensor scales, fp16 q/out, 256 sequences with contexts uniform
+    in 1..2048, stepped over Falcon-7B's 32 layers."""
+    name = "falcon-7b decode step, 32 layers, fp8 KV (MQA)"
+
+    def __init__(self, pa, W, torch, partition_size, args):
+        bs = args.block_size or 16
+        ctx = W.falcon7b_lengths(256)
+        case = W.make_decode_case(f"falcon7b_bs{bs}", "falcon7b", num_seqs=256, num_heads=71,
+                                  num_kv_heads=1, head_dim=64, block_size=bs, context_lens=ctx,
+                                  kv_dtype="fp8_e4m3", q_dtype="f16",
+                                  num_blocks=W.falcon7b_num_blocks(ctx, bs))
+        self.place(torch, case, 32)
+        self.ctx_desc = f"uniform 1..2048, sum {int(self.ctx.sum())}"
+        self.attn_bytes = attention_bytes(self.ctx, self.S, self.H, self.Hkv, self.D, 1, 2, self.bs)
+        self.finish(pa, torch, partition_size, self.ctx.max())
+
+
+class Llama70B(HostLayers):
+    """Llama-2-70B-shaped GQA layer (64 query heads over 8 KV heads of 128, bf16,
+    block 16): 96 independent sequences with log-normal contexts plus 8 groups of
+    4 parallel samples that share a 520-token prompt; every step applies the
+    copy-on-write block copies, the cache write and attention, over L layers."""
+    name = "llama2-70b GQA decode step, bf16 KV, shared-prompt samples"
+
+    def __init__(self, pa, W, torch, partition_size, args):
+        NB = 12288
+        spec = W.llama70b_spec()
+        alloc = pa.BlockAllocator(NB, 16, W.free_order("llama70b", NB))
+        case, pairs = W.shared_prompt_case(alloc, spec, num_blocks=NB)
+        self.place(torch, case, args.layers or 8)
+        self.pairs = pairs
+        P, n_ind = spec.prompt_len, len(spec.independent_ctx)
+        # shared full prompt blocks are read once; every sample owns its copied last block
+        full = (P // 16) * 16
+        shared_extra = (spec.samples - 1) * full * spec.groups
+        self.unique_tokens = int(self.ctx.sum()) - shared_extra
+        self.ctx_desc = (f"96 log-normal median 1024 (128..8192) + 8x4 samples at {P + 1}; "
+                         f"sum {int(self.ctx.sum())}, unique {self.unique_tokens}")
+        self.attn_bytes = attention_bytes(self.ctx, self.S, self.H, self.Hkv, self.D, 2, 2, self.bs,
+                                          unique_tokens=self.unique_tokens)
+        self.logical_attn_bytes = attention_bytes(self.ctx, self.S, self.H, self.Hkv, self.D, 2, 2,
+                                                  self.bs)
+        self.finish(pa, torch, partition_size, self.ctx.max())
+
+
+class Tiny(HostLayers):
+    """The tiny fp32 case: 4 sequences, contexts {5,10,3,16}, 2 heads of 64, block 4."""
+    name = "tiny fp32 decode step, 1 layer"
+
+    def __init__(self, pa, W, torch, partition_size, args):
+        self.place(torch, W.tiny_case(), 1)
+        self.ctx_desc = "5, 10, 3, 16"
+        self.attn_bytes = attention_bytes(self.ctx, self.S, self.H, self.Hkv, self.D, 4, 4, self.bs)
+        self.finish(pa, torch, partition_size, self.ctx.max())
+
+
+WORKLOADS = {"llama7b": Llama7B, "opt13b": Opt13B, "falcon7b": Falcon7B, "llama70b": Llama70B,
+             "tiny": Tiny}
+
+
+def read_traffic(workload, partition_size):
+    """HBM traffic per launch of the dominant kernel from the committed counter
+    summary, if the kernel sources are unchanged since the counters were taken."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.traffic.txt"))):
+        kv = {}
+        for line in open(path):
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("workload") != workload or int(kv.get("partition_size", -1)) != partition_size:
+            continue
+        h = hashlib.sha256()
+        for src in kv["sources"].split():
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() == kv["source_sha256"]:
+            return int(float(kv["traffic_bytes"])), os.path.basename(path)
+    return None, None
+
+
+def calibrate_copy(pa, torch, mib):
+    """One copy_blocks launch moving exactly `mib` MiB (read) + `mib` MiB (write):
+    64 pairs of blocks of mib/64 MiB each (f16 pool of 2*64+ blocks)."""
+    heads = max(1, mib * 1024 * 1024 // 64 // (256 * 128 * 2))       # 64 KiB per (head) row
+    shape = (130, heads, 256, 128)                                     # block = heads x 64 KiB
+    kpool = torch.zeros(shape, dtype=torch.float16, device="cuda")
+    vpool = torch.zeros(shape, dtype=torch.float16, device="cuda")
+    pairs = np.stack([np.arange(64), np.arange(64, 128)], axis=1).astype(np.int32)
+    pa.copy_blocks([kpool], [vpool], pairs)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {mib} MiB read + {mib} MiB written per pool, K and V pools")
 
 
 # ---------------------------------------------------------------- main
@@ -142,6 +336,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU-oracle baseline sample (0 = skip)")
     ap.add_argument("--decode-iters", type=int, default=64)
+    ap.add_argument("--block-size", type=int, default=0, help="falcon7b: block size (default 16)")
+    ap.add_argument("--layers", type=int, default=0, help="llama70b: layers per step (default 8)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch eagerly instead of replaying a captured HIP graph")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first run one plain copy of this many MiB (copy_blocks kernel) so that "
+                         "HBM counters can be scaled by a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path "
@@ -156,36 +357,51 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-    wl = WORKLOADS[args.workload](pa, W, torch, args.partition_size)
+    if args.calibrate_copy_mib > 0:
+        calibrate_copy(pa, torch, args.calibrate_copy_mib)
+    wl = WORKLOADS[args.workload](pa, W, torch, args.partition_size, args)
 
-    for _ in range(args.warmup):
-        wl.step()
+    # one step and one round of decode launches (every layer once), eager or as HIP graphs
+    step_fn = wl.step
+    decode_fn = lambda: [wl.decode(l) for l in range(wl.L)]
+    for _ in range(max(1, args.warmup)):
+        step_fn()
     torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
+    if not args.no_graph:
+        g_step, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            wl.step()
+        with torch.cuda.graph(g_dec):
+            decode_fn()
+        step_fn, decode_fn = g_step.replay, g_dec.replay
+        for _ in range(max(1, args.warmup)):
+            step_fn()
+        torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} steps, graph={not args.no_graph})")
 
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
     for _ in range(args.steps):
-        wl.step()
+        step_fn()
     end.record()
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
 
     # dominant kernel: decode attention alone, back to back over the layers
-    n = args.decode_iters
-    units = wl.num_decode_units()
+    rounds = max(1, args.decode_iters // wl.L)
     start.record()
-    for i in range(n):
-        wl.decode(i % units)
+    for _ in range(rounds):
+        decode_fn()
     end.record()
     torch.cuda.synchronize()
-    decode_ms = start.elapsed_time(end) / n
+    decode_ms = start.elapsed_time(end) / (rounds * wl.L)
     achieved = wl.attn_bytes / (decode_ms * 1e-3) / 1e9
     log(f"decode attention: {decode_ms * 1e3:.1f} us per launch, {achieved:.0f} GB/s")
 
     value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
+    traffic, traffic_src = read_traffic(args.workload, args.partition_size)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -197,25 +413,26 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f32",
         "data": "synthetic",
         "config": wl.config(),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "decode_tokens_per_s": round(wl.seq_layers_per_step / (ms_per_step * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "paged_attention_decode",
                      "avg_launch_us": round(decode_ms * 1e3, 2),
-                     "algorithmic_bytes_per_launch": wl.attn_bytes},
+                     "algorithmic_bytes_per_launch": wl.attn_bytes,
+                     "traffic_source": traffic_src},
         "cpu_baseline": None,
     }
 
     if args.cpu_seconds > 0:
         import oracle
-        done, secs, sample = wl.cpu_sample(oracle, args.cpu_seconds)
+        done, secs, kv_bytes, sample = wl.cpu_sample(oracle, args.cpu_seconds)
         line["cpu_baseline"] = {"value": round(done / secs, 3), "unit": "seq-layers/s",
                                 "cores": 1, "kind": "oracle", "sample": sample,
-                                "gbs_equivalent": round(done * wl.attn_bytes / wl.S / secs / 1e9, 3)}
+                                "kv_gbs_equivalent": round(kv_bytes / secs / 1e9, 3)}
         log(f"cpu oracle: {done} seq-layers in {secs:.1f}s")
     print(json.dumps(line), flush=True)
 
