@@ -1,0 +1,411 @@
+// paged_attention_decode, matrix-core path for grouped heads (2 <= G <= 16
+// query heads per KV head).
+//
+// When several query heads share one KV head (KV 缓存与分页注意力 §11;
+// KV Cache从原理到实战 §5.3), one pass over a KV tile serves all G heads, and
+// scores = K·Q^T and out = P·V become small dense contractions that run on
+// v_mfma_f32_16x16x32_{f16,bf16}: the G heads (padded to 16) are one MFMA
+// dimension, 16 tokens another and head_dim the reduction.
+//
+// A work item = (sequence, KV head, partition), taken from the compact work
+// list of worklist.h; the workgroup's NW wavefronts take interleaved 32-token
+// chunks of it.  Per chunk a wavefront
+//   * loads K rows straight into the MFMA A-operand layout (lane = token row,
+//     eight consecutive head_dim numbers per lane, 16-byte loads) and computes
+//     S^T[token][head] for two 16-token tiles;
+//   * runs the online softmax per head column (running max kept in log2 units,
+//     max shared by the four lanes of a column through two shuffles; the
+//     running sum stays per lane and is added up at the end);
+//   * stages its V rows in its own LDS slice (rows of absent tokens are
+//     zeroed) and reads them back transposed as the A operand of
+//     O^T[d][head] += V^T·P^T, whose B operand is P^T exactly as the score
+//     MFMA left it in registers (for bf16, P is split into a bf16 high and
+//     low part so the weights keep fp32-like precision).
+// The wavefronts' states are merged through LDS (log-sum-exp merge); with
+// several partitions the result goes to the workspace and the reduction
+// kernel of decode.hip finishes it.  An fp8 cache is widened to fp16 in
+// registers (value * 2^-8; the factor is folded into the scales).
+#include "kernels.h"
+#include "pa_device.h"
+#include "worklist.h"
+
+namespace pa {
+namespace {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTableCap = 1024;     // block-table entries staged in LDS per segment
+constexpr int kChunk = 32;                  // tokens per wavefront step (two 16-token tiles)
+constexpr float kNegInf = -__builtin_inff();
+
+struct Op8 {                                // eight 16-bit MFMA operand values
+    uint32_t w[4];
+};
+
+template <int MT>
+__device__ __forceinline__ f32x4 mma(const Op8& a, const Op8& b, f32x4 c) {
+    if constexpr (MT == PA_F16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+    half2_t h;
+    h.x = (_Float16)a;
+    h.y = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, h);
+}
+
+template <int MT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    if constexpr (MT == PA_F16) return pack_f16(a, b);
+    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+}
+
+// head_dim offset of operand chunk c for lane group j (the same mapping is
+// used for K and for Q, so any mapping gives the same dot products; this one
+// makes each lane's loads contiguous within a token row).
+template <int KVDT, int D>
+__device__ __forceinline__ int dmap(int c, int j) {
+    if constexpr (KVDT == PA_FP8_E4M3) return (D / 4) * j + 8 * c;
+    return 32 * c + 8 * j;
+}
+
+template <int KVDT, int QDT, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+    constexpr int MT = (KVDT == PA_FP8_E4M3) ? PA_F16 : KVDT;   // MFMA operand type
+    constexpr int EB = elem_bytes(KVDT);
+    constexpr int NC = D / 32;               // score MFMAs per 16-token tile
+    constexpr int NDT = D / 16;              // output d-tiles
+    constexpr int LDV = D + 8;               // LDS row stride of a staged V tile (halfs)
+    constexpr int PPR = D * EB / 16;         // 16-byte pieces per V row
+    constexpr int NPV = kChunk * PPR / 64;   // V pieces per lane per chunk
+    constexpr int VEL = 16 / EB;             // numbers per V piece
+    constexpr int VTILE = kChunk * LDV;      // halfs of one wavefront's V slice
+    constexpr int NT = NW * 64;
+    constexpr int MERGE_FLOATS = NW * 16 * D + NW * 16 * 2;
+    constexpr int SMEM_HALFS = (NW * VTILE > 2 * MERGE_FLOATS) ? NW * VTILE : 2 * MERGE_FLOATS;
+    static_assert(NPV >= 1 && (kChunk * PPR) % 64 == 0, "V staging split");
+
+    __shared__ int32_t tbl[kTableCap];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_HALFS];
+    __shared__ int32_t pref[kWindow + 1];
+    __shared__ int32_t scan[NT];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int j = lane >> 4;
+    const int c16 = lane & 15;
+    const int G = a.num_heads / a.num_kv_heads;
+    const int bs = 1 << a.log2_bs;
+    uint16_t* vs = smem + wave * VTILE;
+    const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+    const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+    const int64_t row_bytes = (int64_t)D * EB;
+    float* macc = reinterpret_cast<float*>(smem);     // [NW][16][D], after the token loop
+    float* mml = macc + NW * 16 * D;                  // [NW][16][2]
+
+    for (int s0 = 0; s0 < a.num_seqs; s0 += kWindow) {
+        const int nwin = min(kWindow, a.num_seqs - s0);
+        const int total = build_prefix<NT>(a, s0, nwin, pref, scan);
+        const int64_t items = (int64_t)total * a.num_kv_heads;
+        for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
+            const int kvh = (int)(w % a.num_kv_heads);
+            const int gp = (int)(w / a.num_kv_heads);
+            const int sl = locate(pref, nwin, gp);
+            const int s = s0 + sl;
+            const int part = gp - pref[sl];
+            const int ctx = clamp_ctx(a.ctx_lens[s], a.ctx_cap);
+            const int t0 = part * a.part_tokens;
+            const int t1 = min(ctx, t0 + a.part_tokens);
+            const int nparts_s = parts_of(ctx, a.part_tokens);
+
+            // B operand of the score MFMA: Q^T[d][head], head = c16 (zero for padding heads)
+            Op8 qop[NC];
+            {
+                const bool live = c16 < G;
+                const char* qrow = reinterpret_cast<const char*>(a.q) +
+                                   ((int64_t)s * a.num_heads + kvh * G + (live ? c16 : 0)) * D *
+                                       elem_bytes(QDT);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const int d = dmap<KVDT, D>(c, j);
+                    Op8 o{{0u, 0u, 0u, 0u}};
+                    if (live) {
+                        if constexpr (QDT == MT) {
+                            const Raw16 r = load16(qrow + d * 2);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) o.w[q] = r.w[q];
+                        } else {               // bf16 query with an fp16 MFMA: widen then round
+                            float f[8];
+                            unpack16<QDT>(load16(qrow + d * elem_bytes(QDT)), f);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) o.w[q] = pack_f16(f[2 * q], f[2 * q + 1]);
+                        }
+                    }
+                    qop[c] = o;
+                }
+            }
+
+            float m = kNegInf, l = 0.0f;
+            f32x4 acc[NDT];
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+            const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
+            const int b_first = t0 >> a.log2_bs;
+            const int b_end = (t1 + bs - 1) >> a.log2_bs;
+            for (int sb = b_first; sb < b_end; sb += kTableCap) {
+                const int se = min(b_end, sb + kTableCap);
+                __syncthreads();
+                for (int i = threadIdx.x; i < se - sb; i += NT) {
+                    const int b = trow[sb + i];
+                    tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
+                }
+                __syncthreads();
+                const int ts = max(t0, sb << a.log2_bs);
+                const int te = min(t1, se << a.log2_bs);
+
+                // pool row (token row index) of token t, or -1 when absent
+                auto row_of = [&](int t) -> int64_t {
+                    if (t >= te) return -1;
+                    const int blk = tbl[(t >> a.log2_bs) - sb];
+                    if (blk < 0) return -1;
+                    return (((int64_t)blk * a.num_kv_heads + kvh) << a.log2_bs) + (t & (bs - 1));
+                };
+
+                for (int c0 = ts + wave * kChunk; c0 < te; c0 += NW * kChunk) {
+                    // ---- loads: K in A-operand layout, V rows for staging
+                    Op8 kop[2][NC];
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        const int64_t r = row_of(c0 + 16 * tt + c16);
+                        const char* krow = kbase + (r < 0 ? 0 : r) * row_bytes;
+                        if constexpr (KVDT == PA_FP8_E4M3) {
+                            // D/4 contiguous codes per lane: 8 per score MFMA
+#pragma unroll
+                            for (int hh = 0; hh < D / 64; ++hh) {
+                                const Raw16 raw = load16(krow + (D / 4) * j + 16 * hh);
+#pragma unroll
+                                for (int q = 0; q < 2; ++q) {
+                                    Op8& o = kop[tt][2 * hh + q];
+                                    e4m3x4_to_f16x4(raw.w[2 * q], o.w[0], o.w[1]);
+                                    e4m3x4_to_f16x4(raw.w[2 * q + 1], o.w[2], o.w[3]);
+                                }
+                            }
+                        } else {
+#pragma unroll
+                            for (int c = 0; c < NC; ++c) {
+                                const Raw16 raw = load16(krow + dmap<KVDT, D>(c, j) * 2);
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) kop[tt][c].w[q] = raw.w[q];
+                            }
+                        }
+                    }
+                    Raw16 vraw[NPV];
+                    bool vlive[NPV];
+#pragma unroll
+                    for (int u = 0; u < NPV; ++u) {
+                        const int p = u * 64 + lane;
+                        const int64_t r = row_of(c0 + p / PPR);
+                        vlive[u] = r >= 0;
+                        vraw[u] = load16(vbase + (r < 0 ? 0 : r) * row_bytes + (p % PPR) * 16);
+                    }
+
+                    // ---- scores S^T[token][head] for the two tiles
+                    f32x4 sc[2];
+#pragma unroll
+                    for (int tt = 0; tt < 2; ++tt) {
+                        sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int c = 0; c < NC; ++c) sc[tt] = mma<MT>(kop[tt][c], qop[c], sc[tt]);
+                    }
+
+                    // ---- online softmax per head column
+                    float sv[8];
+                    bool live[8];
+                    float mx = kNegInf;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int tt = e >> 2, i = e & 3;
+                        live[e] = row_of(c0 + 16 * tt + 4 * j + i) >= 0;
+                        sv[e] = live[e] ? sc[tt][i] * a.qk_scale : kNegInf;
+                        mx = fmaxf(mx, sv[e]);
+                    }
+                    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                    const float mn = fmaxf(m, mx);
+                    const float alpha = (m == kNegInf) ? 0.0f : fast_exp2(m - mn);
+                    float pr[8];
+                    float psum = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        pr[e] = live[e] ? fast_exp2(sv[e] - mn) : 0.0f;
+                        psum += pr[e];
+                    }
+                    l = l * alpha + psum;
+                    m = mn;
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+                    // P^T as the B operand.  bf16 keeps only 8 significant bits, so there
+                    // P = hi + lo (both bf16) and V·P is taken twice; fp16 P is one operand.
+                    Op8 pop, plo;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) pop.w[q] = pack2<MT>(pr[2 * q], pr[2 * q + 1]);
+                    if constexpr (MT == PA_BF16) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const float h0 = __uint_as_float(pop.w[q] << 16);
+                            const float h1 = __uint_as_float(pop.w[q] & 0xFFFF0000u);
+                            plo.w[q] = pack2<MT>(pr[2 * q] - h0, pr[2 * q + 1] - h1);
+                        }
+                    }
+
+                    // ---- stage V rows (zero for absent tokens), read back transposed
+#pragma unroll
+                    for (int u = 0; u < NPV; ++u) {
+                        const int p = u * 64 + lane;
+                        uint16_t* dst = vs + (p / PPR) * LDV + (p % PPR) * VEL;
+                        if constexpr (KVDT == PA_FP8_E4M3) {
+                            uint32_t wv[8];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) e4m3x4_to_f16x4(vraw[u].w[q], wv[2 * q], wv[2 * q + 1]);
+#pragma unroll
+                            for (int q = 0; q < 8; ++q) wv[q] = vlive[u] ? wv[q] : 0u;
+                            *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
+                            *reinterpret_cast<uint4*>(dst + 8) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
+                        } else {
+                            const uint4 v = vlive[u] ? make_uint4(vraw[u].w[0], vraw[u].w[1],
+                                                                  vraw[u].w[2], vraw[u].w[3])
+                                                     : make_uint4(0u, 0u, 0u, 0u);
+                            *reinterpret_cast<uint4*>(dst) = v;
+                        }
+                    }
+                    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        Op8 vop;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int e0 = 2 * q, e1 = 2 * q + 1;
+                            const int r0 = 16 * (e0 >> 2) + 4 * j + (e0 & 3);
+                            const int r1 = 16 * (e1 >> 2) + 4 * j + (e1 & 3);
+                            const uint32_t lo = vs[r0 * LDV + 16 * dt + c16];
+                            const uint32_t hi = vs[r1 * LDV + 16 * dt + c16];
+                            vop.w[q] = lo | (hi << 16);
+                        }
+                        acc[dt] = mma<MT>(vop, pop, acc[dt]);
+                        if constexpr (MT == PA_BF16) acc[dt] = mma<MT>(vop, plo, acc[dt]);
+                    }
+                    __builtin_amdgcn_wave_barrier();
+                }
+            }
+
+            // ---- per-column totals, then merge the wavefronts through LDS
+            l += __shfl_xor(l, 16, 64);
+            l += __shfl_xor(l, 32, 64);
+            __syncthreads();                                   // V slices are reused below
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                *reinterpret_cast<f32x4*>(macc + (wave * 16 + c16) * D + 16 * dt + 4 * j) = acc[dt];
+            if (j == 0) {
+                mml[(wave * 16 + c16) * 2] = m;
+                mml[(wave * 16 + c16) * 2 + 1] = l;
+            }
+            __syncthreads();
+            if (wave == 0 && c16 < G) {
+                float M = kNegInf;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mml[(ww * 16 + c16) * 2]);
+                float f[NW];
+                float L = 0.0f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) {
+                    const float mw = mml[(ww * 16 + c16) * 2];
+                    f[ww] = (mw == kNegInf) ? 0.0f : fast_exp2(mw - M);
+                    L += f[ww] * mml[(ww * 16 + c16) * 2 + 1];
+                }
+                const int head = kvh * G + c16;
+                const float inv_l = L > 0.0f ? 1.0f / L : 0.0f;
+                const int64_t idx = ((int64_t)s * a.num_heads + head) * a.num_parts + part;
+                const int64_t nslots = (int64_t)a.num_seqs * a.num_heads * a.num_parts;
+                if (nparts_s != 1 && j == 0) {
+                    a.ws[idx] = M;
+                    a.ws[nslots + idx] = L;
+                }
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    float o[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float v = 0.0f;
+#pragma unroll
+                        for (int ww = 0; ww < NW; ++ww)
+                            v += f[ww] * macc[(ww * 16 + c16) * D + 16 * dt + 4 * j + i];
+                        o[i] = v * inv_l;
+                    }
+                    const int d = 16 * dt + 4 * j;
+                    if (nparts_s == 1) {
+                        char* op = reinterpret_cast<char*>(a.out) +
+                                   (((int64_t)s * a.num_heads + head) * D + d) * elem_bytes(QDT);
+                        *reinterpret_cast<uint2*>(op) =
+                            make_uint2(pack2<QDT>(o[0] * a.out_scale, o[1] * a.out_scale),
+                                       pack2<QDT>(o[2] * a.out_scale, o[3] * a.out_scale));
+                    } else {
+                        float* wo = a.ws + 2 * nslots + idx * D + d;
+                        wo[0] = o[0];
+                        wo[1] = o[1];
+                        wo[2] = o[2];
+                        wo[3] = o[3];
+                    }
+                }
+            }
+            __syncthreads();          // LDS is reused by the next item
+        }
+    }
+}
+
+template <int KVDT, int QDT, int D>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+    constexpr int NW = 4;
+    auto kernel = decode_mfma_kernel<KVDT, QDT, D, NW>;
+    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kernel), NW * 64,
+                                         (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NW * 64), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int KVDT, int QDT>
+hipError_t launch_dim(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+    if (head_dim == 64) return launch_typed<KVDT, QDT, 64>(a, stream);
+    if (head_dim == 128) return launch_typed<KVDT, QDT, 128>(a, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool decode_mfma_supported(int q_dt, int kv_dt, int head_dim, int group) {
+    if (group < 2 || group > 16) return false;
+    if (head_dim != 64 && head_dim != 128) return false;
+    if (q_dt != PA_F16 && q_dt != PA_BF16) return false;
+    return kv_dt == q_dt || kv_dt == PA_FP8_E4M3;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+                              hipStream_t stream) {
+    if (kv_dt == PA_F16 && q_dt == PA_F16) return launch_dim<PA_F16, PA_F16>(a, head_dim, stream);
+    if (kv_dt == PA_BF16 && q_dt == PA_BF16) return launch_dim<PA_BF16, PA_BF16>(a, head_dim, stream);
+    if (kv_dt == PA_FP8_E4M3 && q_dt == PA_F16)
+        return launch_dim<PA_FP8_E4M3, PA_F16>(a, head_dim, stream);
+    if (kv_dt == PA_FP8_E4M3 && q_dt == PA_BF16)
+        return launch_dim<PA_FP8_E4M3, PA_BF16>(a, head_dim, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -59,4 +59,9 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                          hipStream_t stream);
 
+// matrix-core kernel for grouped heads (decode_mfma.hip)
+bool decode_mfma_supported(int q_dt, int kv_dt, int head_dim, int group);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+                              hipStream_t stream);
+
 }  // namespace pa

@@ -86,6 +86,20 @@ def assert_pools_equal(dev: DeviceCase, kp: np.ndarray, vp: np.ndarray):
     assert np.array_equal(raw_view(gv, dt), raw_view(vp, dt)), "V pool differs after write"
 
 
-def max_err(got: np.ndarray, ref: np.ndarray) -> float:
+def half_ulp(ref: np.ndarray, dtype: str) -> np.ndarray:
+    """Half a unit in the last place of ``dtype`` at |ref| (normal range)."""
+    bits = {"f32": 24, "f16": 11, "bf16": 8}[dtype]
+    min_exp = {"f32": -126, "f16": -14, "bf16": -126}[dtype]
+    e = np.floor(np.log2(np.maximum(np.abs(ref), 1e-300)))
+    return np.exp2(np.maximum(e, min_exp) - bits)
+
+
+def max_err(got: np.ndarray, ref: np.ndarray, out_dtype: str = None) -> float:
+    """Max-abs error; with ``out_dtype``, beyond the rounding of the exact result to
+    that output format (half an ulp at the reference value), which every correct
+    implementation that stores its result in that format has to make."""
     assert np.isfinite(got).all(), "non-finite output"
-    return float(np.abs(got - ref).max(initial=0.0))
+    err = np.abs(got - ref)
+    if out_dtype is not None:
+        err = np.maximum(err - half_ulp(ref, out_dtype), 0.0)
+    return float(err.max(initial=0.0))

@@ -37,7 +37,7 @@ def run_and_check(case, partitions=(0,), label=""):
     for ps in partitions:
         out = dev.attend(ps, out=torch.empty_like(dev.q))
         torch.cuda.synchronize()
-        errs[ps] = max_err(out_to_f64(out), ref)
+        errs[ps] = max_err(out_to_f64(out), ref, case.q_dtype)
         assert errs[ps] <= TOL[case.kv_dtype], (case.name, ps, errs[ps])
     say(f"    max-abs error by partition size: {errs}")
     return dev, ref
@@ -106,7 +106,7 @@ def test_llama70b_gqa_shared_prompt_cow(full):
     for ps in (0, 512):
         out = dev.attend(ps, out=torch.empty_like(dev.q))
         torch.cuda.synchronize()
-        err = max_err(out_to_f64(out), ref)
+        err = max_err(out_to_f64(out), ref, "bf16")
         say(f"    partition {ps}: max-abs error {err:.3g}")
         assert err <= TOL["bf16"]
 
@@ -152,7 +152,7 @@ def test_llama7b_full_size_sampled():
         got_k = d["k_pool"][blk, :, 15, :].cpu().numpy()
         assert np.array_equal(got_k.view(np.uint16), kp[nblk - 1, :, 15, :].view(np.uint16))
         for ps, o in outs.items():
-            err = float(np.abs(o[s] - ref).max())
+            err = max_err(o[s], ref, "f16")
             say(f"    seq {s} partition {ps}: max-abs error {err:.3g}")
             assert err <= TOL["f16"]
     del d
@@ -196,7 +196,7 @@ def test_empty_batch_and_empty_contexts():
         assert np.array_equal(o[:2], np.zeros_like(o[:2]))
         ref = oracle.paged_attention(case.q, "f16", case.k_pool, case.v_pool, "f16",
                                      case.block_tables, case.context_lens, 16, case.scale)
-        assert max_err(o, ref) <= TOL["f16"]
+        assert max_err(o, ref, "f16") <= TOL["f16"]
 
 
 def test_placement_permutation_is_bit_identical():
@@ -236,7 +236,7 @@ def test_invalid_table_entries_are_never_read():
         K = oracle.gather_sequence(case.k_pool, "f32", good[s], n, 4)[keep]
         V = oracle.gather_sequence(case.v_pool, "f32", good[s], n, 4)[keep]
         ref = oracle.contiguous_attention(Q[s], K, V, case.scale)
-        assert max_err(out[s], ref) <= TOL["f32"]
+        assert max_err(out[s], ref, "f32") <= TOL["f32"]
 
 
 def test_context_clamped_to_max_context_len():
@@ -251,7 +251,7 @@ def test_context_clamped_to_max_context_len():
     torch.cuda.synchronize()
     ref = oracle.paged_attention(case.q, "f16", case.k_pool, case.v_pool, "f16",
                                  case.block_tables, [30, 20], 8, case.scale)
-    assert max_err(out_to_f64(out), ref) <= TOL["f16"]
+    assert max_err(out_to_f64(out), ref, "f16") <= TOL["f16"]
 
 
 # ------------------------------------------------------------------ cache write, block copy
@@ -323,3 +323,47 @@ def test_copy_blocks_bit_exact_many_layers_and_pairs(dt):
     oracle.copy_blocks(pools_np, [tuple(p) for p in pairs])
     for g, r in zip(dev, pools_np):
         assert np.array_equal(W.raw_view(from_dev(g, dt), dt), W.raw_view(r, dt))
+
+
+# ------------------------------------------------------------------ grouped heads (matrix-core path)
+MFMA_CASES = [
+    # kv, q, D, bs, H, Hkv, ctx
+    ("bf16", "bf16", 128, 16, 64, 8, [1, 17, 31, 32, 33, 530, 1000]),
+    ("f16", "f16", 128, 16, 32, 2, [5, 64, 700]),
+    ("f16", "f16", 64, 8, 12, 1, [3, 100, 257]),
+    ("bf16", "bf16", 64, 32, 10, 2, [2, 33, 129]),
+    ("f16", "f16", 128, 64, 6, 2, [65, 128, 400]),
+    ("bf16", "bf16", 128, 4, 8, 4, [9, 50]),
+    ("fp8_e4m3", "f16", 64, 16, 16, 2, [1, 40, 600]),
+    ("fp8_e4m3", "bf16", 128, 16, 16, 2, [7, 300]),
+    ("fp8_e4m3", "f16", 128, 32, 24, 2, [31, 90]),
+    ("f16", "f16", 128, 1, 4, 2, [1, 2, 45]),
+]
+
+
+@pytest.mark.parametrize("kv,q,D,bs,H,Hkv,ctx", MFMA_CASES)
+def test_grouped_heads(kv, q, D, bs, H, Hkv, ctx):
+    case = W.make_decode_case(f"gqa_{kv}_{q}_{D}_{bs}_{H}x{Hkv}", "tiny", num_seqs=len(ctx),
+                              num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                              context_lens=ctx, kv_dtype=kv, q_dtype=q, spare_blocks=7,
+                              salt=H * 7 + bs, max_blocks=int(W.blocks_needed(ctx, bs).max()) + 2)
+    run_and_check(case, partitions=(0, 64, 512))
+
+
+def test_grouped_heads_invalid_table_entries():
+    case = W.make_decode_case("gqa_badtable", "tiny", num_seqs=2, num_heads=16, num_kv_heads=2,
+                              head_dim=128, block_size=16, context_lens=[100, 70], kv_dtype="bf16",
+                              q_dtype="bf16", spare_blocks=3, append=False)
+    good = case.block_tables.copy()
+    case.block_tables[0, 2] = -1
+    case.block_tables[1, 1] = case.num_blocks + 7
+    say("[case] grouped heads, invalid table entries")
+    out = out_to_f64(DeviceCase(case).attend(0))
+    Q = oracle.decode(case.q, "bf16")
+    for s, skip in ((0, 2), (1, 1)):
+        n = int(case.context_lens[s])
+        keep = [t for t in range(n) if t // 16 != skip]
+        K = oracle.gather_sequence(case.k_pool, "bf16", good[s], n, 16)[keep]
+        V = oracle.gather_sequence(case.v_pool, "bf16", good[s], n, 16)[keep]
+        ref = oracle.contiguous_attention(Q[s], K, V, case.scale)
+        assert max_err(out[s], ref, "bf16") <= TOL["bf16"]
