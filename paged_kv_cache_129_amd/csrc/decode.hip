@@ -70,10 +70,12 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
             const int s = s0 + sl;
             const int part = gp - pref[sl];
             const int kvh = h / G;
-            const int ctx = clamp_ctx(a.ctx_lens[s], a.ctx_cap);
+            // first loads of the item, issued together: block-table segment, length, query
             const int t0 = part * a.part_tokens;
-            const int t1 = min(ctx, t0 + a.part_tokens);
-            const int nparts_s = parts_of(ctx, a.part_tokens);
+            const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
+            TablePrefetch<NT, kTableCap> tpre;
+            tpre.issue(trow, t0 >> a.log2_bs, table_span(a, t0, kTableCap));
+            const int ctx_raw = a.ctx_lens[s];
 
             // query slice of this lane, pre-scaled into log2 units
             float qf[VEC];
@@ -87,6 +89,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int i = 0; i < VEC; ++i) qf[i] *= a.qk_scale;
             }
+            __builtin_amdgcn_s_waitcnt(0);
+            const int ctx = clamp_ctx(ctx_raw, a.ctx_cap);
+            const int t1 = min(ctx, t0 + a.part_tokens);
+            const int nparts_s = parts_of(ctx, a.part_tokens);
 
             float m = kNegInf, l = 0.0f;
             float acc[VEC];
@@ -94,15 +100,18 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
             for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
 
             const int64_t head_off = (int64_t)kvh << a.log2_bs;   // token rows within a block
-            const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
             const int b_first = t0 >> a.log2_bs;
             const int b_end = (t1 + bs - 1) >> a.log2_bs;
             for (int sb = b_first; sb < b_end; sb += kTableCap) {
                 const int se = min(b_end, sb + kTableCap);
                 __syncthreads();
-                for (int i = threadIdx.x; i < se - sb; i += NT) {
-                    const int b = trow[sb + i];
-                    tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
+                if (sb == b_first) {
+                    tpre.store(tbl, se - sb, a.num_blocks);
+                } else {
+                    for (int i = threadIdx.x; i < se - sb; i += NT) {
+                        const int b = trow[sb + i];
+                        tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
+                    }
                 }
                 __syncthreads();
                 const int ts = max(t0, sb << a.log2_bs);
@@ -120,8 +129,8 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
                                                          head_off + (t & (bs - 1))
                                                    : 0;
                         const int64_t byte_off = (r * D + col * VEC) * EB;
-                        kr[u] = load16(kbase + byte_off);
-                        vr[u] = load16(vbase + byte_off);
+                        kr[u] = load16_stream(kbase + byte_off);
+                        vr[u] = load16_stream(vbase + byte_off);
                     }
                     float sc[U];
                     float mc = kNegInf;
@@ -357,9 +366,13 @@ int64_t persistent_grid(const void* kernel, int threads, int64_t max_items) {
 hipError_t launch_decode(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                          hipStream_t stream) {
     const int group = a.num_heads / a.num_kv_heads;
-    hipError_t e = decode_mfma_supported(q_dt, kv_dt, head_dim, group)
-                       ? launch_decode_mfma(a, q_dt, kv_dt, head_dim, stream)
-                       : launch_valu(a, q_dt, kv_dt, head_dim, stream);
+    hipError_t e;
+    if (decode_mfma_supported(q_dt, kv_dt, head_dim, group))
+        e = launch_decode_mfma(a, q_dt, kv_dt, head_dim, stream);
+    else if (decode_mqa_supported(q_dt, kv_dt, head_dim, group))
+        e = launch_decode_mqa(a, q_dt, kv_dt, head_dim, stream);
+    else
+        e = launch_valu(a, q_dt, kv_dt, head_dim, stream);
     if (e != hipSuccess || a.num_parts <= 1) return e;
     switch (q_dt) {
         case PA_F32: return launch_reduce<PA_F32>(a, head_dim, stream);

@@ -3,26 +3,28 @@
 //
 // When several query heads share one KV head (KV 缓存与分页注意力 §11;
 // KV Cache从原理到实战 §5.3), one pass over a KV tile serves all G heads, and
-// scores = K·Q^T and out = P·V become small dense contractions that run on
-// v_mfma_f32_16x16x32_{f16,bf16}: the G heads (padded to 16) are one MFMA
-// dimension, 16 tokens another and head_dim the reduction.
+// scores = K·Q^T and out = P·V become small dense contractions on the matrix
+// cores: the G heads (padded to 16) are one MFMA dimension, 16 tokens another.
 //
 // A work item = (sequence, KV head, partition), taken from the compact work
-// list of worklist.h; the workgroup's NW wavefronts take interleaved 32-token
+// list of worklist.h; the workgroup's NW wavefronts take interleaved 16-token
 // chunks of it.  Per chunk a wavefront
-//   * loads K rows straight into the MFMA A-operand layout (lane = token row,
-//     eight consecutive head_dim numbers per lane, 16-byte loads) and computes
-//     S^T[token][head] for two 16-token tiles;
-//   * runs the online softmax per head column (running max kept in log2 units,
-//     max shared by the four lanes of a column through two shuffles; the
-//     running sum stays per lane and is added up at the end);
-//   * stages its V rows in its own LDS slice (rows of absent tokens are
-//     zeroed) and reads them back transposed as the A operand of
-//     O^T[d][head] += V^T·P^T, whose B operand is P^T exactly as the score
-//     MFMA left it in registers (for bf16, P is split into a bf16 high and
-//     low part so the weights keep fp32-like precision).
-// The wavefronts' states are merged through LDS (log-sum-exp merge); with
-// several partitions the result goes to the workspace and the reduction
+//   * loads the 16 K rows straight into the A-operand layout of
+//     v_mfma_f32_16x16x32 (lane = token row, eight consecutive head_dim numbers
+//     per lane, 16-byte loads) and computes S^T[token][head];
+//   * runs the online softmax per head column (running max in log2 units,
+//     shared by a column's four lanes through two shuffles; the running sum
+//     stays per lane and is added up at the end);
+//   * stages its V rows in its own LDS slice (rows of absent tokens zeroed)
+//     and reads them back transposed as the A operand of the K=16 MFMA
+//     O^T[d][head] += V^T·P^T, whose B operand is exactly the register layout
+//     the score MFMA produced (for bf16, P is split into a bf16 high and low
+//     part so the weights keep ~16 significant bits).
+// Everything around the loads is branch-free (masks are selects), which keeps
+// the compiler's wait counts exact; 16-token chunks keep the register budget
+// low enough for four wavefronts per SIMD, whose loads overlap each other's
+// compute.  The wavefronts' states are merged through LDS (log-sum-exp merge);
+// with several partitions the result goes to the workspace and the reduction
 // kernel of decode.hip finishes it.  An fp8 cache is widened to fp16 in
 // registers (value * 2^-8; the factor is folded into the scales).
 #include "kernels.h"
@@ -34,24 +36,40 @@ namespace {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTableCap = 1024;     // block-table entries staged in LDS per segment
-constexpr int kChunk = 32;                  // tokens per wavefront step (two 16-token tiles)
+constexpr int kChunk = 16;          // tokens per wavefront step
 constexpr float kNegInf = -__builtin_inff();
 
-struct Op8 {                                // eight 16-bit MFMA operand values
+struct Op8 {                        // eight 16-bit MFMA operand values
     uint32_t w[4];
+};
+struct Op4 {                        // four 16-bit MFMA operand values
+    uint32_t w[2];
 };
 
 template <int MT>
-__device__ __forceinline__ f32x4 mma(const Op8& a, const Op8& b, f32x4 c) {
+__device__ __forceinline__ f32x4 mma32(const Op8& a, const Op8& b, f32x4 c) {
     if constexpr (MT == PA_F16) {
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
                                                       __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
     } else {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ f32x4 mma16(const Op4& a, const Op4& b, f32x4 c) {
+    if constexpr (MT == PA_F16) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                     __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                         __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
     }
 }
 
@@ -68,9 +86,9 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
     return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
 }
 
-// head_dim offset of operand chunk c for lane group j (the same mapping is
-// used for K and for Q, so any mapping gives the same dot products; this one
-// makes each lane's loads contiguous within a token row).
+// head_dim offset of score-operand chunk c for lane group j (the same mapping
+// is used for K and for Q, so any mapping gives the same dot products; this
+// one makes each lane's loads contiguous within a token row).
 template <int KVDT, int D>
 __device__ __forceinline__ int dmap(int c, int j) {
     if constexpr (KVDT == PA_FP8_E4M3) return (D / 4) * j + 8 * c;
@@ -81,7 +99,7 @@ template <int KVDT, int QDT, int D, int NW>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = (KVDT == PA_FP8_E4M3) ? PA_F16 : KVDT;   // MFMA operand type
     constexpr int EB = elem_bytes(KVDT);
-    constexpr int NC = D / 32;               // score MFMAs per 16-token tile
+    constexpr int NC = D / 32;               // score MFMAs per chunk
     constexpr int NDT = D / 16;              // output d-tiles
     constexpr int LDV = D + 8;               // LDS row stride of a staged V tile (halfs)
     constexpr int PPR = D * EB / 16;         // 16-byte pieces per V row
@@ -121,10 +139,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             const int sl = locate(pref, nwin, gp);
             const int s = s0 + sl;
             const int part = gp - pref[sl];
-            const int ctx = clamp_ctx(a.ctx_lens[s], a.ctx_cap);
+            // first loads of the item, issued together: block-table segment, length, query
             const int t0 = part * a.part_tokens;
-            const int t1 = min(ctx, t0 + a.part_tokens);
-            const int nparts_s = parts_of(ctx, a.part_tokens);
+            const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
+            TablePrefetch<NT, kTableCap> tpre;
+            tpre.issue(trow, t0 >> a.log2_bs, table_span(a, t0, kTableCap));
+            const int ctx_raw = a.ctx_lens[s];
 
             // B operand of the score MFMA: Q^T[d][head], head = c16 (zero for padding heads)
             Op8 qop[NC];
@@ -136,131 +156,143 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     const int d = dmap<KVDT, D>(c, j);
-                    Op8 o{{0u, 0u, 0u, 0u}};
-                    if (live) {
-                        if constexpr (QDT == MT) {
-                            const Raw16 r = load16(qrow + d * 2);
+                    Op8 o;
+                    if constexpr (QDT == MT) {
+                        const Raw16 r = load16(qrow + d * 2);
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) o.w[q] = r.w[q];
-                        } else {               // bf16 query with an fp16 MFMA: widen then round
-                            float f[8];
-                            unpack16<QDT>(load16(qrow + d * elem_bytes(QDT)), f);
+                        for (int q = 0; q < 4; ++q) o.w[q] = live ? r.w[q] : 0u;
+                    } else {                       // bf16 query with an fp16 MFMA: widen then round
+                        float f[8];
+                        unpack16<QDT>(load16(qrow + d * elem_bytes(QDT)), f);
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) o.w[q] = pack_f16(f[2 * q], f[2 * q + 1]);
-                        }
+                        for (int q = 0; q < 4; ++q) o.w[q] = live ? pack_f16(f[2 * q], f[2 * q + 1]) : 0u;
                     }
                     qop[c] = o;
                 }
             }
+            // settle the one-time loads here: the wait-count analysis cannot see across
+            // the token loop's back edge that they completed
+            __builtin_amdgcn_s_waitcnt(0);
+            const int ctx = clamp_ctx(ctx_raw, a.ctx_cap);
+            const int t1 = min(ctx, t0 + a.part_tokens);
+            const int nparts_s = parts_of(ctx, a.part_tokens);
 
             float m = kNegInf, l = 0.0f;
             f32x4 acc[NDT];
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-            const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
             const int b_first = t0 >> a.log2_bs;
             const int b_end = (t1 + bs - 1) >> a.log2_bs;
             for (int sb = b_first; sb < b_end; sb += kTableCap) {
                 const int se = min(b_end, sb + kTableCap);
                 __syncthreads();
-                for (int i = threadIdx.x; i < se - sb; i += NT) {
-                    const int b = trow[sb + i];
-                    tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
+                if (sb == b_first) {
+                    tpre.store(tbl, se - sb, a.num_blocks);
+                } else {
+                    for (int i = threadIdx.x; i < se - sb; i += NT) {
+                        const int b = trow[sb + i];
+                        tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
+                    }
                 }
                 __syncthreads();
                 const int ts = max(t0, sb << a.log2_bs);
                 const int te = min(t1, se << a.log2_bs);
 
-                // pool row (token row index) of token t, or -1 when absent
+                // pool row (token row index) of token t, or -1 when absent; branch-free,
+                // so that loads issued around it keep precise wait counts
                 auto row_of = [&](int t) -> int64_t {
-                    if (t >= te) return -1;
-                    const int blk = tbl[(t >> a.log2_bs) - sb];
-                    if (blk < 0) return -1;
-                    return (((int64_t)blk * a.num_kv_heads + kvh) << a.log2_bs) + (t & (bs - 1));
+                    const bool in = t < te;
+                    const int blk = tbl[in ? (t >> a.log2_bs) - sb : 0];
+                    const int64_t r = (((int64_t)blk * a.num_kv_heads + kvh) << a.log2_bs) + (t & (bs - 1));
+                    return (in && blk >= 0) ? r : (int64_t)-1;
                 };
 
-                for (int c0 = ts + wave * kChunk; c0 < te; c0 += NW * kChunk) {
-                    // ---- loads: K in A-operand layout, V rows for staging
-                    Op8 kop[2][NC];
-#pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        const int64_t r = row_of(c0 + 16 * tt + c16);
+                // One chunk's K operands and raw V pieces.  Two sets alternate: the next
+                // chunk's loads are always issued (past the end they read row 0 and are
+                // masked) before the current chunk is computed, so they overlap it and
+                // no branch sits between a load and its wait.
+                struct ChunkRegs {
+                    Op8 k[NC];
+                    Raw16 v[NPV];
+                    bool vlive[NPV];
+                };
+                auto load_chunk = [&](ChunkRegs& R, int c0) {
+                    {
+                        const int64_t r = row_of(c0 + c16);
                         const char* krow = kbase + (r < 0 ? 0 : r) * row_bytes;
                         if constexpr (KVDT == PA_FP8_E4M3) {
-                            // D/4 contiguous codes per lane: 8 per score MFMA
 #pragma unroll
                             for (int hh = 0; hh < D / 64; ++hh) {
-                                const Raw16 raw = load16(krow + (D / 4) * j + 16 * hh);
+                                const Raw16 raw = load16_stream(krow + (D / 4) * j + 16 * hh);
+                                // keep the raw codes; widened when used
 #pragma unroll
-                                for (int q = 0; q < 2; ++q) {
-                                    Op8& o = kop[tt][2 * hh + q];
-                                    e4m3x4_to_f16x4(raw.w[2 * q], o.w[0], o.w[1]);
-                                    e4m3x4_to_f16x4(raw.w[2 * q + 1], o.w[2], o.w[3]);
-                                }
+                                for (int q = 0; q < 4; ++q) R.k[2 * hh + (q >> 1)].w[(q & 1) * 2] = raw.w[q];
                             }
                         } else {
 #pragma unroll
                             for (int c = 0; c < NC; ++c) {
-                                const Raw16 raw = load16(krow + dmap<KVDT, D>(c, j) * 2);
+                                const Raw16 raw = load16_stream(krow + dmap<KVDT, D>(c, j) * 2);
 #pragma unroll
-                                for (int q = 0; q < 4; ++q) kop[tt][c].w[q] = raw.w[q];
+                                for (int q = 0; q < 4; ++q) R.k[c].w[q] = raw.w[q];
                             }
                         }
                     }
-                    Raw16 vraw[NPV];
-                    bool vlive[NPV];
 #pragma unroll
                     for (int u = 0; u < NPV; ++u) {
                         const int p = u * 64 + lane;
                         const int64_t r = row_of(c0 + p / PPR);
-                        vlive[u] = r >= 0;
-                        vraw[u] = load16(vbase + (r < 0 ? 0 : r) * row_bytes + (p % PPR) * 16);
+                        R.vlive[u] = r >= 0;
+                        R.v[u] = load16_stream(vbase + (r < 0 ? 0 : r) * row_bytes + (p % PPR) * 16);
                     }
-
-                    // ---- scores S^T[token][head] for the two tiles
-                    f32x4 sc[2];
+                };
+                auto compute_chunk = [&](ChunkRegs& R, int c0) {
+                    Op8 kop[NC];
 #pragma unroll
-                    for (int tt = 0; tt < 2; ++tt) {
-                        sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int c = 0; c < NC; ++c) sc[tt] = mma<MT>(kop[tt][c], qop[c], sc[tt]);
+                    for (int c = 0; c < NC; ++c) {
+                        if constexpr (KVDT == PA_FP8_E4M3) {
+                            e4m3x4_to_f16x4(R.k[c].w[0], kop[c].w[0], kop[c].w[1]);
+                            e4m3x4_to_f16x4(R.k[c].w[2], kop[c].w[2], kop[c].w[3]);
+                        } else {
+                            kop[c] = R.k[c];
+                        }
                     }
+                    // ---- scores S^T[token][head]
+                    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < NC; ++c) sc = mma32<MT>(kop[c], qop[c], sc);
 
                     // ---- online softmax per head column
-                    float sv[8];
-                    bool live[8];
+                    float sv[4];
+                    bool live[4];
                     float mx = kNegInf;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int tt = e >> 2, i = e & 3;
-                        live[e] = row_of(c0 + 16 * tt + 4 * j + i) >= 0;
-                        sv[e] = live[e] ? sc[tt][i] * a.qk_scale : kNegInf;
-                        mx = fmaxf(mx, sv[e]);
+                    for (int i = 0; i < 4; ++i) {
+                        live[i] = row_of(c0 + 4 * j + i) >= 0;
+                        sv[i] = live[i] ? sc[i] * a.qk_scale : kNegInf;
+                        mx = fmaxf(mx, sv[i]);
                     }
                     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
                     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
                     const float mn = fmaxf(m, mx);
                     const float alpha = (m == kNegInf) ? 0.0f : fast_exp2(m - mn);
-                    float pr[8];
+                    float pr[4];
                     float psum = 0.0f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        pr[e] = live[e] ? fast_exp2(sv[e] - mn) : 0.0f;
-                        psum += pr[e];
+                    for (int i = 0; i < 4; ++i) {
+                        pr[i] = live[i] ? fast_exp2(sv[i] - mn) : 0.0f;
+                        psum += pr[i];
                     }
                     l = l * alpha + psum;
                     m = mn;
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-                    // P^T as the B operand.  bf16 keeps only 8 significant bits, so there
-                    // P = hi + lo (both bf16) and V·P is taken twice; fp16 P is one operand.
-                    Op8 pop, plo;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) pop.w[q] = pack2<MT>(pr[2 * q], pr[2 * q + 1]);
+                    Op4 pop, plo;
+                    pop.w[0] = pack2<MT>(pr[0], pr[1]);
+                    pop.w[1] = pack2<MT>(pr[2], pr[3]);
                     if constexpr (MT == PA_BF16) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
+                        for (int q = 0; q < 2; ++q) {
                             const float h0 = __uint_as_float(pop.w[q] << 16);
                             const float h1 = __uint_as_float(pop.w[q] & 0xFFFF0000u);
                             plo.w[q] = pack2<MT>(pr[2 * q] - h0, pr[2 * q + 1] - h1);
@@ -275,35 +307,41 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                         if constexpr (KVDT == PA_FP8_E4M3) {
                             uint32_t wv[8];
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) e4m3x4_to_f16x4(vraw[u].w[q], wv[2 * q], wv[2 * q + 1]);
+                            for (int q = 0; q < 4; ++q) e4m3x4_to_f16x4(R.v[u].w[q], wv[2 * q], wv[2 * q + 1]);
 #pragma unroll
-                            for (int q = 0; q < 8; ++q) wv[q] = vlive[u] ? wv[q] : 0u;
+                            for (int q = 0; q < 8; ++q) wv[q] = R.vlive[u] ? wv[q] : 0u;
                             *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
                             *reinterpret_cast<uint4*>(dst + 8) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
                         } else {
-                            const uint4 v = vlive[u] ? make_uint4(vraw[u].w[0], vraw[u].w[1],
-                                                                  vraw[u].w[2], vraw[u].w[3])
-                                                     : make_uint4(0u, 0u, 0u, 0u);
-                            *reinterpret_cast<uint4*>(dst) = v;
+                            uint32_t wv[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) wv[q] = R.vlive[u] ? R.v[u].w[q] : 0u;
+                            *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
                         }
                     }
                     __builtin_amdgcn_wave_barrier();
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
-                        Op8 vop;
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int e0 = 2 * q, e1 = 2 * q + 1;
-                            const int r0 = 16 * (e0 >> 2) + 4 * j + (e0 & 3);
-                            const int r1 = 16 * (e1 >> 2) + 4 * j + (e1 & 3);
-                            const uint32_t lo = vs[r0 * LDV + 16 * dt + c16];
-                            const uint32_t hi = vs[r1 * LDV + 16 * dt + c16];
-                            vop.w[q] = lo | (hi << 16);
-                        }
-                        acc[dt] = mma<MT>(vop, pop, acc[dt]);
-                        if constexpr (MT == PA_BF16) acc[dt] = mma<MT>(vop, plo, acc[dt]);
+                        const uint16_t* col = vs + 4 * j * LDV + 16 * dt + c16;
+                        Op4 vop;
+                        vop.w[0] = (uint32_t)col[0] | ((uint32_t)col[LDV] << 16);
+                        vop.w[1] = (uint32_t)col[2 * LDV] | ((uint32_t)col[3 * LDV] << 16);
+                        acc[dt] = mma16<MT>(vop, pop, acc[dt]);
+                        if constexpr (MT == PA_BF16) acc[dt] = mma16<MT>(vop, plo, acc[dt]);
                     }
                     __builtin_amdgcn_wave_barrier();
+                };
+
+                constexpr int kStep = NW * kChunk;
+                ChunkRegs ra, rb;
+                int c0 = ts + wave * kChunk;
+                load_chunk(ra, c0);
+                for (; c0 < te; c0 += 2 * kStep) {
+                    load_chunk(rb, c0 + kStep);
+                    compute_chunk(ra, c0);
+                    if (c0 + kStep >= te) break;
+                    load_chunk(ra, c0 + 2 * kStep);
+                    compute_chunk(rb, c0 + kStep);
                 }
             }
 

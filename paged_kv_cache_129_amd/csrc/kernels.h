@@ -64,4 +64,9 @@ bool decode_mfma_supported(int q_dt, int kv_dt, int head_dim, int group);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                               hipStream_t stream);
 
+// matrix-core kernel for large groups, G > 16 (decode_mqa.hip)
+bool decode_mqa_supported(int q_dt, int kv_dt, int head_dim, int group);
+hipError_t launch_decode_mqa(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+                             hipStream_t stream);
+
 }  // namespace pa

@@ -35,6 +35,16 @@ __device__ __forceinline__ Raw16 load16(const void* p) {
     return Raw16{{v.x, v.y, v.z, v.w}};
 }
 
+// Streaming (non-temporal) 16-byte load for K/V cache reads: every cached
+// byte is read once per decode step, and on gfx950 this cache policy moves
+// markedly more bytes per second than the default one (measured 7.06 vs
+// 6.35 TB/s for a plain read kernel).
+__device__ __forceinline__ Raw16 load16_stream(const void* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return Raw16{{v.x, v.y, v.z, v.w}};
+}
+
 __device__ __forceinline__ void store16(void* p, const Raw16& r) {
     *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
 }

@@ -65,6 +65,39 @@ __device__ __forceinline__ int locate(const int32_t* pref, int n, int gp) {
     return lo;
 }
 
+// Block-table entries of an item's first table segment, loaded by the
+// workgroup's threads together with the item's other first loads (length,
+// query) so that starting an item costs one memory round trip, then stored to
+// LDS once the length is known.  Entries are read at indices clamped to the
+// span, which lies inside the sequence's table row.
+template <int NT, int CAP>
+struct TablePrefetch {
+    static constexpr int TP = (CAP + NT - 1) / NT;
+    int32_t v[TP];
+    __device__ __forceinline__ void issue(const int32_t* trow, int b_first, int span) {
+#pragma unroll
+        for (int k = 0; k < TP; ++k) {
+            const int i = k * NT + (int)threadIdx.x;
+            v[k] = trow[b_first + min(i, span - 1)];
+        }
+    }
+    __device__ __forceinline__ void store(int32_t* tbl, int n, int num_blocks) const {
+#pragma unroll
+        for (int k = 0; k < TP; ++k) {
+            const int i = k * NT + (int)threadIdx.x;
+            if (i < n) tbl[i] = (v[k] >= 0 && v[k] < num_blocks) ? v[k] : -1;
+        }
+    }
+};
+
+// Table entries [b_first, b_first + span) hold every block a partition that
+// starts at token t0 can touch (bounded by the table row and by CAP).
+__device__ __forceinline__ int table_span(const DecodeArgs& a, int t0, int cap) {
+    const int b_first = t0 >> a.log2_bs;
+    const int b_last = (int)(((int64_t)t0 + a.part_tokens + (1 << a.log2_bs) - 1) >> a.log2_bs);
+    return max(1, min(min(cap, a.max_blocks - b_first), b_last - b_first));
+}
+
 // Grid for a persistent decode kernel: no more workgroups than items, no
 // more than the device holds at once, a multiple of 8 when that is possible.
 int64_t persistent_grid(const void* kernel, int threads, int64_t max_items);

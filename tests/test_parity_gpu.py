@@ -338,6 +338,14 @@ MFMA_CASES = [
     ("fp8_e4m3", "bf16", 128, 16, 16, 2, [7, 300]),
     ("fp8_e4m3", "f16", 128, 32, 24, 2, [31, 90]),
     ("f16", "f16", 128, 1, 4, 2, [1, 2, 45]),
+    # G > 16: one wavefront per 16-head tile, shared LDS staging
+    ("fp8_e4m3", "f16", 64, 16, 71, 1, [1, 2, 31, 32, 33, 700, 2048]),
+    ("fp8_e4m3", "bf16", 64, 8, 71, 1, [5, 100, 513]),
+    ("f16", "f16", 128, 16, 64, 2, [17, 300]),
+    ("bf16", "bf16", 128, 32, 64, 1, [1, 64, 200]),
+    ("bf16", "bf16", 64, 16, 20, 1, [9, 77]),
+    ("f16", "f16", 64, 64, 128, 1, [3, 130]),
+    ("fp8_e4m3", "f16", 128, 16, 100, 1, [40, 129]),
 ]
 
 
