@@ -64,8 +64,9 @@ class Workload:
         self.pa, self.torch = pa, torch
         self.partition_size = partition_size
         self.max_ctx = int(max_ctx)
-        ws = pa.paged_attention_workspace_size(self.S, self.H, self.D, self.max_ctx, partition_size)
-        self.ws = torch.empty(max(ws, 256), dtype=torch.uint8, device="cuda")
+        ws = pa.paged_attention_workspace_size(self.S, self.H, self.Hkv, self.D, self.max_ctx,
+                                               partition_size)
+        self.ws = pa.new_workspace(ws, "cuda")
         for d in self.layers:
             d.setdefault("out", torch.empty_like(d["q"]))
         self.step_bytes = self.L * (self.attn_bytes + self.write_bytes) + \

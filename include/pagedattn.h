@@ -100,13 +100,18 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dt
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                             int32_t num_blocks, float k_scale, float v_scale, void* stream);
 
+/* partition_size value that selects the balanced split (see below) */
+#define PA_PARTITION_BALANCED (-1)
+
 /*
  * Workspace bytes needed by pa_paged_attention_decode with the same
- * arguments (0 when partition_size == 0 or every sequence fits one
- * partition).  Returns 0 for invalid sizes.
+ * arguments: 0 for a single pass (partition_size == 0) or when every
+ * sequence fits one partition.  The balanced split's size depends on the
+ * compute-unit count of the current device.  Returns 0 for invalid sizes.
  */
-size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                         int32_t max_context_len, int32_t partition_size);
+size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_context_len,
+                                         int32_t partition_size);
 
 /*
  * paged_attention_decode — one decode step of attention over a paged cache.
@@ -137,10 +142,16 @@ size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, in
  *                  > 0: split-context — each sequence is cut into partitions
  *                  of that many tokens, each partition produces (max, sum,
  *                  output) partials in `workspace`, and a log-sum-exp
- *                  reduction kernel merges them.  Results agree with the
- *                  single pass within rounding.
+ *                  reduction kernel merges them.
+ *                  PA_PARTITION_BALANCED: the batch's contexts, laid end to
+ *                  end, are cut into one equal token range per workgroup of
+ *                  a launch that fills the GPU; contexts cut by a range
+ *                  boundary are merged by the same log-sum-exp reduction.
+ *                  Every mode gives the single pass's result within rounding.
  *   workspace      DEVICE, >= pa_paged_attention_workspace_size(...) bytes,
- *                  256-byte aligned; may be NULL when that size is 0.
+ *                  256-byte aligned, no initial contents; may be NULL when
+ *                  that size is 0.  Calls that share a workspace must be
+ *                  ordered (one stream, or synchronised).
  * Limits: head_dim in {64, 128}; block_size a power of two in [1, 256];
  * num_heads % num_kv_heads == 0; num_seqs * num_heads * partitions < 2^31.
  */

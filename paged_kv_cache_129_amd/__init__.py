@@ -39,7 +39,7 @@ _SIGNATURES = [
      [_vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
       ctypes.c_float, ctypes.c_float, _vp]),
-    ("pa_paged_attention_workspace_size", ctypes.c_size_t, [ctypes.c_int32] * 5),
+    ("pa_paged_attention_workspace_size", ctypes.c_size_t, [ctypes.c_int32] * 6),
     ("pa_paged_attention_decode", ctypes.c_int32,
      [_vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp,
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -157,10 +157,19 @@ def kv_cache_write(k_new, v_new, k_pool, v_pool, slot_mapping, *, k_scale: float
            "kv_cache_write")
 
 
-def paged_attention_workspace_size(num_seqs: int, num_heads: int, head_dim: int,
-                                   max_context_len: int, partition_size: int) -> int:
-    return int(lib.pa_paged_attention_workspace_size(num_seqs, num_heads, head_dim,
+PARTITION_BALANCED = -1
+
+
+def paged_attention_workspace_size(num_seqs: int, num_heads: int, num_kv_heads: int,
+                                   head_dim: int, max_context_len: int,
+                                   partition_size: int) -> int:
+    return int(lib.pa_paged_attention_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
                                                      max_context_len, partition_size))
+
+
+def new_workspace(nbytes: int, device):
+    """Device workspace of at least ``nbytes`` (never empty; no initial contents needed)."""
+    return _torch().empty(max(int(nbytes), 256), dtype=_torch().uint8, device=device)
 
 
 def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, *,
@@ -177,9 +186,9 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, *
         raise ValueError("block_tables must be int32 [S, max_blocks]")
     if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
         raise ValueError("context_lens must be int32 [S]")
-    need = paged_attention_workspace_size(S, H, D, max_context_len, partition_size)
+    need = paged_attention_workspace_size(S, H, Hkv, D, max_context_len, partition_size)
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = new_workspace(need, q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.pa_paged_attention_decode(

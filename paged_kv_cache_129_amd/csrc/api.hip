@@ -54,6 +54,30 @@ size_t partial_bytes(int64_t num_seqs, int64_t num_heads, int64_t head_dim, int6
     return (b + 255) & ~(size_t)255;
 }
 
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Balanced split: partial records for two slots per (window, worker) and the
+// workers' range descriptors, for the most workers a launch can have on the
+// current device.
+size_t balanced_record_bytes(int64_t num_seqs, int64_t group, int64_t head_dim) {
+    const int64_t windows = (num_seqs + pa::kWindow - 1) / pa::kWindow;
+    const int64_t workers = (int64_t)pa::device_cus() * pa::balanced_workers_per_cu((int)group);
+    return round256((size_t)(windows * workers * 2 * group) * (size_t)(head_dim + 2) * sizeof(float));
+}
+size_t balanced_desc_bytes(int64_t num_seqs) {
+    const int64_t windows = (num_seqs + pa::kWindow - 1) / pa::kWindow;
+    const int64_t workers = (int64_t)pa::device_cus() * pa::balanced_workers_per_cu(1);
+    return round256((size_t)(windows * workers) * pa::kDescWords * sizeof(int64_t));
+}
+
+// group of query heads one work unit covers: all of a KV head's query heads
+// for the grouped kernels, one head for the per-head kernel
+int64_t unit_group(int32_t num_heads, int32_t num_kv_heads) {
+    return num_kv_heads > 0 && num_heads % num_kv_heads == 0 && num_heads / num_kv_heads >= 2
+               ? num_heads / num_kv_heads
+               : 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,11 +144,15 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dt
     return launch_checked([&] { return pa::launch_kv_write(a, src_dtype, kv_dtype, as_stream(stream)); });
 }
 
-size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
-                                         int32_t max_context_len, int32_t partition_size) {
-    if (num_seqs <= 0 || num_heads <= 0 || head_dim <= 0 || max_context_len < 0 ||
-        partition_size < 0)
+size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_context_len,
+                                         int32_t partition_size) {
+    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+        max_context_len < 0 || (partition_size < 0 && partition_size != PA_PARTITION_BALANCED))
         return 0;
+    if (partition_size == PA_PARTITION_BALANCED)
+        return balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads), head_dim) +
+               balanced_desc_bytes(num_seqs);
     return partial_bytes(num_seqs, num_heads, head_dim,
                          num_partitions(max_context_len, partition_size));
 }
@@ -140,7 +168,8 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
                                     size_t workspace_bytes, void* stream) {
     if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype)) return PA_ERR_INVALID_ARG;
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
-        num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 || partition_size < 0)
+        num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
+        (partition_size < 0 && partition_size != PA_PARTITION_BALANCED))
         return PA_ERR_INVALID_ARG;
     if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
     const int lbs = log2_exact(block_size);
@@ -160,9 +189,14 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
 
     const int64_t cap64 = std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq << lbs);
     const int32_t ctx_cap = (int32_t)std::min<int64_t>(cap64, INT32_MAX);
-    const int64_t parts = num_partitions(ctx_cap, partition_size);
+    const bool balanced = partition_size == PA_PARTITION_BALANCED;
+    const int64_t parts = balanced ? 1 : num_partitions(ctx_cap, partition_size);
     if ((int64_t)num_seqs * num_heads * parts >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
-    const size_t need = partial_bytes(num_seqs, num_heads, head_dim, parts);
+    const size_t rec_bytes =
+        balanced ? balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads), head_dim)
+                 : partial_bytes(num_seqs, num_heads, head_dim, parts);
+    const size_t need =
+        rec_bytes + (balanced ? balanced_desc_bytes(num_seqs) : 0);
     if (need > 0 && (!workspace || workspace_bytes < need ||
                      (reinterpret_cast<uintptr_t>(workspace) & 255u)))
         return PA_ERR_WORKSPACE;
@@ -175,6 +209,9 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
     a.tables = block_tables;
     a.ctx_lens = context_lens;
     a.ws = reinterpret_cast<float*>(workspace);
+    a.nrec = (int64_t)num_seqs * num_heads * parts;     // balanced: set with the grid
+    a.desc = balanced ? reinterpret_cast<int64_t*>(reinterpret_cast<char*>(workspace) + rec_bytes)
+                      : nullptr;
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
@@ -183,7 +220,7 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
     a.num_blocks = num_blocks;
     a.log2_bs = lbs;
     a.num_parts = (int32_t)parts;
-    a.part_tokens = parts > 1 ? partition_size : std::max<int32_t>(ctx_cap, 1);
+    a.part_tokens = balanced ? -1 : (parts > 1 ? partition_size : std::max<int32_t>(ctx_cap, 1));
     const float kfac = kv_dtype == PA_FP8_E4M3 ? k_scale * pa::dequant_factor(kv_dtype) : 1.0f;
     const float vfac = kv_dtype == PA_FP8_E4M3 ? v_scale * pa::dequant_factor(kv_dtype) : 1.0f;
     a.qk_scale = scale * pa::kLog2e * kfac;

@@ -44,11 +44,9 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
     constexpr int NT = NW * 64;
     static_assert(LPR >= 4 && LPR <= 32, "row split");
 
-    __shared__ int32_t tbl[kTableCap];
-    __shared__ float merge_ml[NW][2];
-    __shared__ float merge_acc[NW][D];
-    __shared__ int32_t pref[kWindow + 1];
-    __shared__ int32_t scan[NT];
+    constexpr int WT = kTableCap / NW;       // block-table entries staged per wavefront
+    __shared__ int32_t tbl_all[NW][WT];
+    __shared__ __attribute__((aligned(8))) int32_t wl_lds[kListInts];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -58,24 +56,22 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
     const int G = a.num_heads / a.num_kv_heads;
     const char* kbase = reinterpret_cast<const char*>(a.k_pool);
     const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+    int32_t* tbl = tbl_all[wave];
 
+    Schedule<NT> sch;
     for (int s0 = 0; s0 < a.num_seqs; s0 += kWindow) {
-        const int nwin = min(kWindow, a.num_seqs - s0);
-        const int total = build_prefix<NT>(a, s0, nwin, pref, scan);
-        const int64_t items = (int64_t)total * a.num_heads;
-        for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
-            const int h = (int)(w % a.num_heads);
-            const int gp = (int)(w / a.num_heads);
-            const int sl = locate(pref, nwin, gp);
-            const int s = s0 + sl;
-            const int part = gp - pref[sl];
+        sch.build(a, s0, min(kWindow, a.num_seqs - s0), a.num_heads, wl_lds,
+                  blockIdx.x * NW + wave, gridDim.x * NW, lane == 0);
+        Item itm;
+        while (sch.next(a, itm)) {
+            const int s = itm.s;
+            const int h = itm.unit;
             const int kvh = h / G;
-            // first loads of the item, issued together: block-table segment, length, query
-            const int t0 = part * a.part_tokens;
+            // first loads of the item, issued together: block-table segment, query
+            const int t0 = itm.t0, t1 = itm.t1;
             const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
-            TablePrefetch<NT, kTableCap> tpre;
-            tpre.issue(trow, t0 >> a.log2_bs, table_span(a, t0, kTableCap));
-            const int ctx_raw = a.ctx_lens[s];
+            TablePrefetch<64, WT> tpre;
+            tpre.issue(trow, t0 >> a.log2_bs, table_span(a, t0, t1, WT), a.max_blocks, lane);
 
             // query slice of this lane, pre-scaled into log2 units
             float qf[VEC];
@@ -90,9 +86,6 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
                 for (int i = 0; i < VEC; ++i) qf[i] *= a.qk_scale;
             }
             __builtin_amdgcn_s_waitcnt(0);
-            const int ctx = clamp_ctx(ctx_raw, a.ctx_cap);
-            const int t1 = min(ctx, t0 + a.part_tokens);
-            const int nparts_s = parts_of(ctx, a.part_tokens);
 
             float m = kNegInf, l = 0.0f;
             float acc[VEC];
@@ -102,21 +95,21 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
             const int64_t head_off = (int64_t)kvh << a.log2_bs;   // token rows within a block
             const int b_first = t0 >> a.log2_bs;
             const int b_end = (t1 + bs - 1) >> a.log2_bs;
-            for (int sb = b_first; sb < b_end; sb += kTableCap) {
-                const int se = min(b_end, sb + kTableCap);
-                __syncthreads();
+            for (int sb = b_first; sb < b_end; sb += WT) {
+                const int se = min(b_end, sb + WT);
+                __builtin_amdgcn_wave_barrier();
                 if (sb == b_first) {
-                    tpre.store(tbl, se - sb, a.num_blocks);
+                    tpre.store(tbl, se - sb, a.num_blocks, lane);
                 } else {
-                    for (int i = threadIdx.x; i < se - sb; i += NT) {
+                    for (int i = lane; i < se - sb; i += 64) {
                         const int b = trow[sb + i];
                         tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
                     }
                 }
-                __syncthreads();
+                __builtin_amdgcn_wave_barrier();
                 const int ts = max(t0, sb << a.log2_bs);
                 const int te = min(t1, se << a.log2_bs);
-                for (int c = ts + wave * CH; c < te; c += NW * CH) {
+                for (int c = ts; c < te; c += CH) {
                     Raw16 kr[U], vr[U];
                     bool valid[U];
 #pragma unroll
@@ -184,121 +177,146 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
                 m = mn;
             }
 
-            // merge the workgroup's wavefronts through LDS
+            // this wavefront's result for its item (lanes of row 0 hold it)
             if (row == 0) {
+                const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+                if (itm.whole) {
 #pragma unroll
-                for (int i = 0; i < VEC; ++i) merge_acc[wave][col * VEC + i] = acc[i];
-                if (col == 0) {
-                    merge_ml[wave][0] = m;
-                    merge_ml[wave][1] = l;
-                }
-            }
-            __syncthreads();
-            if (wave == 0 && row == 0) {
-                float M = kNegInf;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, merge_ml[ww][0]);
-                float L = 0.0f;
-                float o[VEC];
-#pragma unroll
-                for (int i = 0; i < VEC; ++i) o[i] = 0.0f;
-                if (M != kNegInf) {
-#pragma unroll
-                    for (int ww = 0; ww < NW; ++ww) {
-                        const float mw = merge_ml[ww][0];
-                        const float f = (mw == kNegInf) ? 0.0f : fast_exp2(mw - M);
-                        L += merge_ml[ww][1] * f;
-#pragma unroll
-                        for (int i = 0; i < VEC; ++i) o[i] += merge_acc[ww][col * VEC + i] * f;
-                    }
-                }
-                const float inv_l = L > 0.0f ? 1.0f / L : 0.0f;
-                if (nparts_s == 1) {
-#pragma unroll
-                    for (int i = 0; i < VEC; ++i) o[i] *= inv_l * a.out_scale;
+                    for (int i = 0; i < VEC; ++i) acc[i] *= inv_l * a.out_scale;
                     char* op = reinterpret_cast<char*>(a.out) +
                                (((int64_t)s * a.num_heads + h) * D + col * VEC) * elem_bytes(QDT);
-                    store_vals<QDT>(op, o, VEC);
+                    store_vals<QDT>(op, acc, VEC);
                 } else {
-                    const int64_t idx = ((int64_t)s * a.num_heads + h) * a.num_parts + part;
-                    const int64_t nslots = (int64_t)a.num_seqs * a.num_heads * a.num_parts;
+                    const int64_t r = itm.rec0;
                     if (col == 0) {
-                        a.ws[idx] = M;
-                        a.ws[nslots + idx] = L;
+                        a.ws[r] = m;
+                        a.ws[a.nrec + r] = l;
                     }
 #pragma unroll
-                    for (int i = 0; i < VEC; ++i) a.ws[2 * nslots + idx * D + col * VEC + i] = o[i] * inv_l;
+                    for (int i = 0; i < VEC; ++i) a.ws[2 * a.nrec + r * D + col * VEC + i] = acc[i] * inv_l;
                 }
             }
-            __syncthreads();          // merge buffers are reused by the next item
         }
     }
 }
 
-// Merge the partitions of every (sequence, head) that has more than one:
-// out = sum_p w_p o_p / sum_p w_p with w_p = 2^(m_p - max m) l_p.
+template <int QDT>
+__device__ __forceinline__ void store_one(void* out, int64_t i, float v) {
+    if constexpr (QDT == PA_F32) {
+        reinterpret_cast<float*>(out)[i] = v;
+    } else if constexpr (QDT == PA_F16) {
+        reinterpret_cast<_Float16*>(out)[i] = (_Float16)v;
+    } else {
+        reinterpret_cast<uint16_t*>(out)[i] = (uint16_t)f32_to_bf16_bits(v);
+    }
+}
+
+// Log-sum-exp merge of n partial records (m, l, o) of one head, for this
+// lane's D/64 dimensions: out = sum_k w_k o_k / sum_k w_k with
+// w_k = 2^(m_k - max m) l_k, accumulated online (the running maximum rescales
+// what is already summed).  Records are fetched kMergeBatch at a time so that
+// their loads overlap; `rec(k)` is the index of the k-th record.
+constexpr int kMergeBatch = 8;
+template <int QDT, int D, typename Rec>
+__device__ __forceinline__ void merge_records(const DecodeArgs& a, int n, Rec rec, int64_t out_row) {
+    constexpr int PER = D / 64;
+    const int lane = threadIdx.x & 63;
+    float M = kNegInf, den = 0.0f, num[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) num[j] = 0.0f;
+    for (int k0 = 0; k0 < n; k0 += kMergeBatch) {
+        float mv[kMergeBatch], lv[kMergeBatch], ov[kMergeBatch][PER];
+#pragma unroll
+        for (int q = 0; q < kMergeBatch; ++q) {
+            const int64_t r = rec(min(k0 + q, n - 1));
+            mv[q] = a.ws[r];
+            lv[q] = a.ws[a.nrec + r];
+#pragma unroll
+            for (int j = 0; j < PER; ++j) ov[q][j] = a.ws[2 * a.nrec + r * D + j * 64 + lane];
+        }
+#pragma unroll
+        for (int q = 0; q < kMergeBatch; ++q) {
+            if (k0 + q < n && mv[q] != kNegInf) {
+                const float Mn = fmaxf(M, mv[q]);
+                const float sc = (M == kNegInf) ? 0.0f : fast_exp2(M - Mn);
+                const float w = fast_exp2(mv[q] - Mn) * lv[q];
+                den = den * sc + w;
+#pragma unroll
+                for (int j = 0; j < PER; ++j) num[j] = num[j] * sc + w * ov[q][j];
+                M = Mn;
+            }
+        }
+    }
+    const float f = den > 0.0f ? a.out_scale / den : 0.0f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) store_one<QDT>(a.out, out_row * D + j * 64 + lane, num[j] * f);
+}
+
+// Partitions: merge the partitions of every (sequence, head) that has more
+// than one; one wavefront per (sequence, head).
 template <int QDT, int D>
 __global__ __launch_bounds__(64) void lse_reduce_kernel(DecodeArgs a) {
-    constexpr int PER = D / 64;
     const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
-    const int64_t nslots = pairs * a.num_parts;
     for (int64_t sh = blockIdx.x; sh < pairs; sh += gridDim.x) {
         const int s = (int)(sh / a.num_heads);
         const int np = parts_of(clamp_ctx(a.ctx_lens[s], a.ctx_cap), a.part_tokens);
-        if (np <= 1) continue;                         // written by the main kernel
-        const float* ws_m = a.ws + sh * a.num_parts;
-        const float* ws_l = a.ws + nslots + sh * a.num_parts;
-        const float* ws_o = a.ws + 2 * nslots + sh * a.num_parts * D;
-        float M = kNegInf;
-        for (int p = 0; p < np; ++p) M = fmaxf(M, ws_m[p]);
-        float num[PER], den = 0.0f;
-#pragma unroll
-        for (int j = 0; j < PER; ++j) num[j] = 0.0f;
-        if (M != kNegInf) {
-            for (int p = 0; p < np; ++p) {
-                const float mp = ws_m[p];
-                const float w = (mp == kNegInf) ? 0.0f : fast_exp2(mp - M) * ws_l[p];
-                den += w;
-#pragma unroll
-                for (int j = 0; j < PER; ++j) num[j] += w * ws_o[p * D + j * 64 + threadIdx.x];
-            }
-        }
-        const float f = den > 0.0f ? a.out_scale / den : 0.0f;
-        char* op = reinterpret_cast<char*>(a.out) + sh * D * elem_bytes(QDT);
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const float v = num[j] * f;
-            const int d = j * 64 + threadIdx.x;
-            if constexpr (QDT == PA_F32) {
-                reinterpret_cast<float*>(op)[d] = v;
-            } else if constexpr (QDT == PA_F16) {
-                reinterpret_cast<_Float16*>(op)[d] = (_Float16)v;
-            } else {
-                reinterpret_cast<uint16_t*>(op)[d] = (uint16_t)f32_to_bf16_bits(v);
-            }
-        }
+        if (np <= 1) continue;                         // written by the attention kernel
+        merge_records<QDT, D>(a, np, [&](int k) { return sh * a.num_parts + k; }, sh);
+    }
+}
+
+// Balanced split: merge every segment whose tokens a worker range boundary
+// cuts.  The worker whose range starts inside the segment's tokens and reaches
+// past their end holds the last piece; its descriptor names the segment, and
+// the pieces are held by workers first..b (first: slot 1 unless its range
+// starts exactly at the segment, every other one: slot 0).  One wavefront per
+// (worker, head of a unit); most find that their worker ends no cut segment.
+template <int QDT, int D>
+__global__ __launch_bounds__(1024) void split_reduce_kernel(DecodeArgs a) {
+    const int64_t windows = (a.num_seqs + kWindow - 1) / kWindow;
+    const int G = a.num_heads / a.units;
+    const int64_t total = windows * a.workers * G;
+    const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
+    for (int64_t x = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); x < total;
+         x += waves) {
+        const int64_t wb = x / G;
+        const int i = (int)(x % G);
+        const int64_t* d = a.desc + wb * kDescWords;
+        const int64_t t0 = d[1], range = d[3];
+        const int64_t run = split_run((int)d[4]);
+        const int64_t win = wb / a.workers, b = wb % a.workers;
+        if (t0 <= 0 || t0 >= run) continue;             // no cut tokens end in this range
+        const int64_t start = b * range - t0;           // the segment's first token, range space
+        if (start + run > (b + 1) * range) continue;    // a later range holds the last piece
+        const int64_t first = start / range;
+        const int s = (int)(d[0] & 0xFFFFFFFF), unit = (int)(d[0] >> 32);
+        auto rec = [&](int k) -> int64_t {
+            const int64_t w = first + k;
+            return ((win * a.workers + w) * 2 + (w * range >= start ? 0 : 1)) * G + i;
+        };
+        merge_records<QDT, D>(a, (int)(b - first + 1), rec,
+                              (int64_t)s * a.num_heads + (int64_t)unit * G + i);
     }
 }
 
 template <int KVDT, int QDT, int D>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
     constexpr int NW = 4;
     constexpr int U = 4;
     auto kernel = decode_valu_kernel<KVDT, QDT, D, NW, U>;
-    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kernel), NW * 64,
-                                         (int64_t)a.num_seqs * a.num_heads * a.num_parts);
+    const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), NW * 64, a.num_heads, 1, a);
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int KVDT, int QDT>
-hipError_t launch_dim(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+hipError_t launch_dim(DecodeArgs& a, int head_dim, hipStream_t stream) {
     if (head_dim == 64) return launch_typed<KVDT, QDT, 64>(a, stream);
     if (head_dim == 128) return launch_typed<KVDT, QDT, 128>(a, stream);
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_valu(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+hipError_t launch_valu(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                        hipStream_t stream) {
     if (kv_dt == q_dt) {
         switch (kv_dt) {
@@ -317,7 +335,17 @@ hipError_t launch_valu(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
 }
 
 template <int QDT>
-hipError_t launch_reduce(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+hipError_t launch_reduce(DecodeArgs& a, int head_dim, hipStream_t stream) {
+    if (a.part_tokens < 0) {
+        const int64_t waves = (a.num_seqs + kWindow - 1) / kWindow * (int64_t)a.workers *
+                              (a.num_heads / a.units);
+        auto k = head_dim == 64 ? split_reduce_kernel<QDT, 64> : split_reduce_kernel<QDT, 128>;
+        // large workgroups: most wavefronts only read one descriptor, and
+        // dispatching many small workgroups would cost more than their work
+        const int64_t grid = persistent_grid(reinterpret_cast<const void*>(k), 1024, (waves + 15) / 16);
+        hipLaunchKernelGGL(k, dim3((uint32_t)grid), dim3(1024), 0, stream, a);
+        return hipGetLastError();
+    }
     const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;
     if (head_dim == 64) {
         auto k = lse_reduce_kernel<QDT, 64>;
@@ -363,7 +391,39 @@ int64_t persistent_grid(const void* kernel, int threads, int64_t max_items) {
     return g;
 }
 
-hipError_t launch_decode(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+int device_cus() {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    std::lock_guard<std::mutex> g(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+        cus = 256;
+    cache.emplace(dev, cus);
+    return cus;
+}
+
+int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers, DecodeArgs& a) {
+    a.units = units;
+    const int per_wg = wave_workers ? threads / 64 : 1;
+    int64_t grid;
+    if (a.part_tokens < 0) {
+        const int64_t cap = (int64_t)device_cus() * balanced_workers_per_cu(a.num_heads / units) / per_wg;
+        grid = persistent_grid(kernel, threads, cap);
+        const int64_t windows = (a.num_seqs + kWindow - 1) / kWindow;
+        a.nrec = windows * grid * per_wg * 2 * (a.num_heads / units);
+    } else {
+        grid = persistent_grid(kernel, threads, ((int64_t)a.num_seqs * units * a.num_parts + per_wg - 1) / per_wg);
+    }
+    a.workers = (int32_t)(grid * per_wg);
+    return grid;
+}
+
+hipError_t launch_decode(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                          hipStream_t stream) {
     const int group = a.num_heads / a.num_kv_heads;
     hipError_t e;
@@ -373,7 +433,7 @@ hipError_t launch_decode(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
         e = launch_decode_mqa(a, q_dt, kv_dt, head_dim, stream);
     else
         e = launch_valu(a, q_dt, kv_dt, head_dim, stream);
-    if (e != hipSuccess || a.num_parts <= 1) return e;
+    if (e != hipSuccess || (a.part_tokens >= 0 && a.num_parts <= 1)) return e;
     switch (q_dt) {
         case PA_F32: return launch_reduce<PA_F32>(a, head_dim, stream);
         case PA_F16: return launch_reduce<PA_F16>(a, head_dim, stream);

@@ -107,14 +107,12 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int VEL = 16 / EB;             // numbers per V piece
     constexpr int VTILE = kChunk * LDV;      // halfs of one wavefront's V slice
     constexpr int NT = NW * 64;
-    constexpr int MERGE_FLOATS = NW * 16 * D + NW * 16 * 2;
-    constexpr int SMEM_HALFS = (NW * VTILE > 2 * MERGE_FLOATS) ? NW * VTILE : 2 * MERGE_FLOATS;
+    constexpr int WT = kTableCap / NW;       // block-table entries staged per wavefront
     static_assert(NPV >= 1 && (kChunk * PPR) % 64 == 0, "V staging split");
 
-    __shared__ int32_t tbl[kTableCap];
-    __shared__ __attribute__((aligned(16))) uint16_t smem[SMEM_HALFS];
-    __shared__ int32_t pref[kWindow + 1];
-    __shared__ int32_t scan[NT];
+    __shared__ int32_t tbl_all[NW][WT];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NW * VTILE];
+    __shared__ __attribute__((aligned(8))) int32_t wl_lds[kListInts];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -123,28 +121,24 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     const int G = a.num_heads / a.num_kv_heads;
     const int bs = 1 << a.log2_bs;
     uint16_t* vs = smem + wave * VTILE;
+    int32_t* tbl = tbl_all[wave];
     const char* kbase = reinterpret_cast<const char*>(a.k_pool);
     const char* vbase = reinterpret_cast<const char*>(a.v_pool);
     const int64_t row_bytes = (int64_t)D * EB;
-    float* macc = reinterpret_cast<float*>(smem);     // [NW][16][D], after the token loop
-    float* mml = macc + NW * 16 * D;                  // [NW][16][2]
 
+    Schedule<NT> sch;
     for (int s0 = 0; s0 < a.num_seqs; s0 += kWindow) {
-        const int nwin = min(kWindow, a.num_seqs - s0);
-        const int total = build_prefix<NT>(a, s0, nwin, pref, scan);
-        const int64_t items = (int64_t)total * a.num_kv_heads;
-        for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
-            const int kvh = (int)(w % a.num_kv_heads);
-            const int gp = (int)(w / a.num_kv_heads);
-            const int sl = locate(pref, nwin, gp);
-            const int s = s0 + sl;
-            const int part = gp - pref[sl];
-            // first loads of the item, issued together: block-table segment, length, query
-            const int t0 = part * a.part_tokens;
+        sch.build(a, s0, min(kWindow, a.num_seqs - s0), a.num_kv_heads, wl_lds,
+                  blockIdx.x * NW + wave, gridDim.x * NW, lane == 0);
+        Item itm;
+        while (sch.next(a, itm)) {
+            const int s = itm.s;
+            const int kvh = itm.unit;
+            // first loads of the item, issued together: block-table segment, query
+            const int t0 = itm.t0, t1 = itm.t1;
             const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
-            TablePrefetch<NT, kTableCap> tpre;
-            tpre.issue(trow, t0 >> a.log2_bs, table_span(a, t0, kTableCap));
-            const int ctx_raw = a.ctx_lens[s];
+            TablePrefetch<64, WT> tpre;
+            tpre.issue(trow, t0 >> a.log2_bs, table_span(a, t0, t1, WT), a.max_blocks, lane);
 
             // B operand of the score MFMA: Q^T[d][head], head = c16 (zero for padding heads)
             Op8 qop[NC];
@@ -173,9 +167,6 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             // settle the one-time loads here: the wait-count analysis cannot see across
             // the token loop's back edge that they completed
             __builtin_amdgcn_s_waitcnt(0);
-            const int ctx = clamp_ctx(ctx_raw, a.ctx_cap);
-            const int t1 = min(ctx, t0 + a.part_tokens);
-            const int nparts_s = parts_of(ctx, a.part_tokens);
 
             float m = kNegInf, l = 0.0f;
             f32x4 acc[NDT];
@@ -184,18 +175,18 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 
             const int b_first = t0 >> a.log2_bs;
             const int b_end = (t1 + bs - 1) >> a.log2_bs;
-            for (int sb = b_first; sb < b_end; sb += kTableCap) {
-                const int se = min(b_end, sb + kTableCap);
-                __syncthreads();
+            for (int sb = b_first; sb < b_end; sb += WT) {
+                const int se = min(b_end, sb + WT);
+                __builtin_amdgcn_wave_barrier();
                 if (sb == b_first) {
-                    tpre.store(tbl, se - sb, a.num_blocks);
+                    tpre.store(tbl, se - sb, a.num_blocks, lane);
                 } else {
-                    for (int i = threadIdx.x; i < se - sb; i += NT) {
+                    for (int i = lane; i < se - sb; i += 64) {
                         const int b = trow[sb + i];
                         tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
                     }
                 }
-                __syncthreads();
+                __builtin_amdgcn_wave_barrier();
                 const int ts = max(t0, sb << a.log2_bs);
                 const int te = min(t1, se << a.log2_bs);
 
@@ -332,9 +323,9 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                     __builtin_amdgcn_wave_barrier();
                 };
 
-                constexpr int kStep = NW * kChunk;
+                constexpr int kStep = kChunk;
                 ChunkRegs ra, rb;
-                int c0 = ts + wave * kChunk;
+                int c0 = ts;
                 load_chunk(ra, c0);
                 for (; c0 < te; c0 += 2 * kStep) {
                     load_chunk(rb, c0 + kStep);
@@ -345,82 +336,49 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                 }
             }
 
-            // ---- per-column totals, then merge the wavefronts through LDS
+            // ---- per-column totals, then this wavefront's result for its item
             l += __shfl_xor(l, 16, 64);
             l += __shfl_xor(l, 32, 64);
-            __syncthreads();                                   // V slices are reused below
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-                *reinterpret_cast<f32x4*>(macc + (wave * 16 + c16) * D + 16 * dt + 4 * j) = acc[dt];
-            if (j == 0) {
-                mml[(wave * 16 + c16) * 2] = m;
-                mml[(wave * 16 + c16) * 2 + 1] = l;
-            }
-            __syncthreads();
-            if (wave == 0 && c16 < G) {
-                float M = kNegInf;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) M = fmaxf(M, mml[(ww * 16 + c16) * 2]);
-                float f[NW];
-                float L = 0.0f;
-#pragma unroll
-                for (int ww = 0; ww < NW; ++ww) {
-                    const float mw = mml[(ww * 16 + c16) * 2];
-                    f[ww] = (mw == kNegInf) ? 0.0f : fast_exp2(mw - M);
-                    L += f[ww] * mml[(ww * 16 + c16) * 2 + 1];
-                }
+            if (c16 < G) {
                 const int head = kvh * G + c16;
-                const float inv_l = L > 0.0f ? 1.0f / L : 0.0f;
-                const int64_t idx = ((int64_t)s * a.num_heads + head) * a.num_parts + part;
-                const int64_t nslots = (int64_t)a.num_seqs * a.num_heads * a.num_parts;
-                if (nparts_s != 1 && j == 0) {
-                    a.ws[idx] = M;
-                    a.ws[nslots + idx] = L;
+                const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
+                const int64_t r = itm.rec0 + (int64_t)c16 * itm.rec_stride;
+                if (!itm.whole && j == 0) {
+                    a.ws[r] = m;
+                    a.ws[a.nrec + r] = l;
                 }
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
-                    float o[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float v = 0.0f;
-#pragma unroll
-                        for (int ww = 0; ww < NW; ++ww)
-                            v += f[ww] * macc[(ww * 16 + c16) * D + 16 * dt + 4 * j + i];
-                        o[i] = v * inv_l;
-                    }
                     const int d = 16 * dt + 4 * j;
-                    if (nparts_s == 1) {
+                    if (itm.whole) {
+                        const float f = inv_l * a.out_scale;
                         char* op = reinterpret_cast<char*>(a.out) +
                                    (((int64_t)s * a.num_heads + head) * D + d) * elem_bytes(QDT);
                         *reinterpret_cast<uint2*>(op) =
-                            make_uint2(pack2<QDT>(o[0] * a.out_scale, o[1] * a.out_scale),
-                                       pack2<QDT>(o[2] * a.out_scale, o[3] * a.out_scale));
+                            make_uint2(pack2<QDT>(acc[dt][0] * f, acc[dt][1] * f),
+                                       pack2<QDT>(acc[dt][2] * f, acc[dt][3] * f));
                     } else {
-                        float* wo = a.ws + 2 * nslots + idx * D + d;
-                        wo[0] = o[0];
-                        wo[1] = o[1];
-                        wo[2] = o[2];
-                        wo[3] = o[3];
+                        float* wo = a.ws + 2 * a.nrec + r * D + d;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) wo[i] = acc[dt][i] * inv_l;
                     }
                 }
             }
-            __syncthreads();          // LDS is reused by the next item
         }
     }
 }
 
 template <int KVDT, int QDT, int D>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
     constexpr int NW = 4;
     auto kernel = decode_mfma_kernel<KVDT, QDT, D, NW>;
-    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kernel), NW * 64,
-                                         (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
+    const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), NW * 64, a.num_kv_heads, 1, a);
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int KVDT, int QDT>
-hipError_t launch_dim(const DecodeArgs& a, int head_dim, hipStream_t stream) {
+hipError_t launch_dim(DecodeArgs& a, int head_dim, hipStream_t stream) {
     if (head_dim == 64) return launch_typed<KVDT, QDT, 64>(a, stream);
     if (head_dim == 128) return launch_typed<KVDT, QDT, 128>(a, stream);
     return hipErrorInvalidValue;
@@ -435,7 +393,7 @@ bool decode_mfma_supported(int q_dt, int kv_dt, int head_dim, int group) {
     return kv_dt == q_dt || kv_dt == PA_FP8_E4M3;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+hipError_t launch_decode_mfma(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                               hipStream_t stream) {
     if (kv_dt == PA_F16 && q_dt == PA_F16) return launch_dim<PA_F16, PA_F16>(a, head_dim, stream);
     if (kv_dt == PA_BF16 && q_dt == PA_BF16) return launch_dim<PA_BF16, PA_BF16>(a, head_dim, stream);

@@ -76,8 +76,7 @@ __global__ __launch_bounds__(HT * 64) void decode_mqa_kernel(DecodeArgs a) {
     __shared__ int32_t tbl[kTableCap];
     __shared__ __attribute__((aligned(16))) uint16_t kst[2][KBUF];
     __shared__ __attribute__((aligned(16))) uint16_t vst[2][VBUF];
-    __shared__ int32_t pref[kWindow + 1];
-    __shared__ int32_t scan[NT];
+    __shared__ __attribute__((aligned(8))) int32_t wl_lds[kListInts];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -89,22 +88,20 @@ __global__ __launch_bounds__(HT * 64) void decode_mqa_kernel(DecodeArgs a) {
     const char* vbase = reinterpret_cast<const char*>(a.v_pool);
     const int64_t row_bytes = (int64_t)D * EB;
 
+    Schedule<NT> sch;
     for (int s0 = 0; s0 < a.num_seqs; s0 += kWindow) {
-        const int nwin = min(kWindow, a.num_seqs - s0);
-        const int total = build_prefix<NT>(a, s0, nwin, pref, scan);
-        const int64_t items = (int64_t)total * a.num_kv_heads;
-        for (int64_t w = blockIdx.x; w < items; w += gridDim.x) {
-            const int kvh = (int)(w % a.num_kv_heads);
-            const int gp = (int)(w / a.num_kv_heads);
-            const int sl = locate(pref, nwin, gp);
-            const int s = s0 + sl;
-            const int part = gp - pref[sl];
-            // first loads of the item, issued together: block-table segment, length, query
-            const int t0 = part * a.part_tokens;
+        sch.build(a, s0, min(kWindow, a.num_seqs - s0), a.num_kv_heads, wl_lds, blockIdx.x,
+                  gridDim.x, threadIdx.x == 0);
+        Item itm;
+        while (sch.next(a, itm)) {
+            const int s = itm.s;
+            const int kvh = itm.unit;
+            // first loads of the item, issued together: block-table segment, query
+            const int t0 = itm.t0, t1 = itm.t1;
             const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
             TablePrefetch<NT, kTableCap> tpre;
-            tpre.issue(trow, t0 >> a.log2_bs, table_span(a, t0, kTableCap));
-            const int ctx_raw = a.ctx_lens[s];
+            tpre.issue(trow, t0 >> a.log2_bs, table_span(a, t0, t1, kTableCap), a.max_blocks,
+                       threadIdx.x);
             const int hl = wave * 16 + c16;            // head within the group
             const bool head_live = hl < G;
 
@@ -137,9 +134,6 @@ __global__ __launch_bounds__(HT * 64) void decode_mqa_kernel(DecodeArgs a) {
             // the token loop's back edge that they completed, and would otherwise wait
             // for every outstanding load (the prefetches too) at the first score MFMA
             __builtin_amdgcn_s_waitcnt(0);
-            const int ctx = clamp_ctx(ctx_raw, a.ctx_cap);
-            const int t1 = min(ctx, t0 + a.part_tokens);
-            const int nparts_s = parts_of(ctx, a.part_tokens);
 
             float m = kNegInf, l = 0.0f;
             f32x4 acc[NDT];
@@ -152,7 +146,7 @@ __global__ __launch_bounds__(HT * 64) void decode_mqa_kernel(DecodeArgs a) {
                 const int se = min(b_end, sb + kTableCap);
                 __syncthreads();
                 if (sb == b_first) {
-                    tpre.store(tbl, se - sb, a.num_blocks);
+                    tpre.store(tbl, se - sb, a.num_blocks, threadIdx.x);
                 } else {
                     for (int i = threadIdx.x; i < se - sb; i += NT) {
                         const int b = trow[sb + i];
@@ -308,16 +302,15 @@ __global__ __launch_bounds__(HT * 64) void decode_mqa_kernel(DecodeArgs a) {
             if (head_live) {
                 const int head = kvh * G + hl;
                 const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
-                const int64_t idx = ((int64_t)s * a.num_heads + head) * a.num_parts + part;
-                const int64_t nslots = (int64_t)a.num_seqs * a.num_heads * a.num_parts;
-                if (nparts_s != 1 && j == 0) {
-                    a.ws[idx] = m;
-                    a.ws[nslots + idx] = l;
+                const int64_t r = itm.rec0 + (int64_t)hl * itm.rec_stride;
+                if (!itm.whole && j == 0) {
+                    a.ws[r] = m;
+                    a.ws[a.nrec + r] = l;
                 }
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
                     const int d = 16 * dt + 4 * j;
-                    if (nparts_s == 1) {
+                    if (itm.whole) {
                         const float f = inv_l * a.out_scale;
                         char* op = reinterpret_cast<char*>(a.out) +
                                    (((int64_t)s * a.num_heads + head) * D + d) * elem_bytes(QDT);
@@ -325,7 +318,7 @@ __global__ __launch_bounds__(HT * 64) void decode_mqa_kernel(DecodeArgs a) {
                             make_uint2(pack2<QDT>(acc[dt][0] * f, acc[dt][1] * f),
                                        pack2<QDT>(acc[dt][2] * f, acc[dt][3] * f));
                     } else {
-                        float* wo = a.ws + 2 * nslots + idx * D + d;
+                        float* wo = a.ws + 2 * a.nrec + r * D + d;
 #pragma unroll
                         for (int i = 0; i < 4; ++i) wo[i] = acc[dt][i] * inv_l;
                     }
@@ -337,16 +330,15 @@ __global__ __launch_bounds__(HT * 64) void decode_mqa_kernel(DecodeArgs a) {
 }
 
 template <int KVDT, int QDT, int D, int HT>
-hipError_t launch_ht(const DecodeArgs& a, hipStream_t stream) {
+hipError_t launch_ht(DecodeArgs& a, hipStream_t stream) {
     auto kernel = decode_mqa_kernel<KVDT, QDT, D, HT>;
-    const int64_t grid = persistent_grid(reinterpret_cast<const void*>(kernel), HT * 64,
-                                         (int64_t)a.num_seqs * a.num_kv_heads * a.num_parts);
+    const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), HT * 64, a.num_kv_heads, 0, a);
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(HT * 64), 0, stream, a);
     return hipGetLastError();
 }
 
 template <int KVDT, int QDT, int D>
-hipError_t launch_d(const DecodeArgs& a, int group, hipStream_t stream) {
+hipError_t launch_d(DecodeArgs& a, int group, hipStream_t stream) {
     const int tiles = (group + 15) / 16;
     if (tiles <= 2) return launch_ht<KVDT, QDT, D, 2>(a, stream);
     if (tiles <= 4) return launch_ht<KVDT, QDT, D, 4>(a, stream);
@@ -355,7 +347,7 @@ hipError_t launch_d(const DecodeArgs& a, int group, hipStream_t stream) {
 }
 
 template <int KVDT, int QDT>
-hipError_t launch_t(const DecodeArgs& a, int head_dim, int group, hipStream_t stream) {
+hipError_t launch_t(DecodeArgs& a, int head_dim, int group, hipStream_t stream) {
     if (head_dim == 64) return launch_d<KVDT, QDT, 64>(a, group, stream);
     return launch_d<KVDT, QDT, 128>(a, group, stream);
 }
@@ -369,7 +361,7 @@ bool decode_mqa_supported(int q_dt, int kv_dt, int head_dim, int group) {
     return kv_dt == q_dt || kv_dt == PA_FP8_E4M3;
 }
 
-hipError_t launch_decode_mqa(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+hipError_t launch_decode_mqa(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                              hipStream_t stream) {
     const int group = a.num_heads / a.num_kv_heads;
     if (kv_dt == PA_F16 && q_dt == PA_F16) return launch_t<PA_F16, PA_F16>(a, head_dim, group, stream);

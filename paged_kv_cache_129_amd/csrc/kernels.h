@@ -36,6 +36,17 @@ struct CopyArgs {
 };
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 
+// Sequences are scheduled in windows of kWindow (their metadata is staged in
+// LDS).  The balanced schedule gives each worker (a wavefront or a workgroup)
+// two partial-record slots and one range descriptor per window; a launch has
+// at most balanced_workers_per_cu(group) workers per CU, so that the workspace
+// can be sized before the kernel is chosen.
+constexpr int kWindow = 1024;
+constexpr int kDescWords = 6;
+// 32 wavefronts per CU at most; the large-group kernel's workers are
+// workgroups of at least two wavefronts
+__host__ __device__ constexpr int balanced_workers_per_cu(int group) { return group > 16 ? 16 : 32; }
+
 struct DecodeArgs {
     const void* q;
     void* out;
@@ -43,7 +54,11 @@ struct DecodeArgs {
     const void* v_pool;
     const int32_t* tables;
     const int32_t* ctx_lens;
-    float* ws;                  // partials when num_parts > 1
+    float* ws;                  // partial records: m[nrec], l[nrec], o[nrec][head_dim]
+    int64_t nrec;               // partial records in ws (set with the grid when balanced)
+    int64_t* desc;              // balanced: 4 words per (window, workgroup) for the reduction
+    int32_t units;              // work units per sequence: query heads or KV heads (set at launch)
+    int32_t workers;            // workers of the attention launch (set at launch)
     int32_t num_seqs;
     int32_t num_heads;
     int32_t num_kv_heads;
@@ -51,22 +66,30 @@ struct DecodeArgs {
     int32_t ctx_cap;            // min(max_context_len, max_blocks * block_size)
     int32_t num_blocks;
     int32_t log2_bs;
-    int32_t part_tokens;        // tokens per partition (>= ctx_cap for a single pass)
-    int32_t num_parts;          // partitions per (sequence, head) in the launch grid
+    int32_t part_tokens;        // tokens per partition (>= ctx_cap for a single pass);
+                                // negative: balanced split
+    int32_t num_parts;          // partitions per (sequence, head); 1 when balanced
     float qk_scale;             // softmax scale * log2(e) * K dequant factor
     float out_scale;            // V dequant factor
 };
-hipError_t launch_decode(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+
+// compute units of the current device (cached per device)
+int device_cus();
+// Grid of an attention launch with `units` work units per sequence, whose
+// workers are wavefronts (wave_workers) or workgroups; records the worker
+// count (and, when balanced, the partial-record count) in `a`.
+int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers, DecodeArgs& a);
+hipError_t launch_decode(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                          hipStream_t stream);
 
 // matrix-core kernel for grouped heads (decode_mfma.hip)
 bool decode_mfma_supported(int q_dt, int kv_dt, int head_dim, int group);
-hipError_t launch_decode_mfma(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+hipError_t launch_decode_mfma(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                               hipStream_t stream);
 
 // matrix-core kernel for large groups, G > 16 (decode_mqa.hip)
 bool decode_mqa_supported(int q_dt, int kv_dt, int head_dim, int group);
-hipError_t launch_decode_mqa(const DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+hipError_t launch_decode_mqa(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                              hipStream_t stream);
 
 }  // namespace pa

@@ -81,6 +81,9 @@ def decode_call(**kw):
     (dict(max_blocks=0), -1),
     (dict(part=-16), -1),
     (dict(part=16), -8),                    # split needs a workspace
+    (dict(part=-1), -8),                    # so does the balanced split
+    (dict(part=-1, ws=ctypes.c_void_p(0x1010), ws_bytes=1 << 30), -8),   # misaligned
+    (dict(part=-2), -1),                    # -1 is the only negative partition size
     (dict(part=16, ws=ctypes.c_void_p(0x1000), ws_bytes=10), -8),
 ])
 def test_decode_validation(kw, status):
@@ -92,10 +95,28 @@ def test_decode_zero_sequences_is_noop():
 
 
 def test_workspace_size():
-    assert pa.paged_attention_workspace_size(4, 8, 128, 100, 0) == 0
-    assert pa.paged_attention_workspace_size(4, 8, 128, 512, 512) == 0
-    n = pa.paged_attention_workspace_size(4, 8, 128, 1025, 512)
-    assert n >= 4 * 8 * 3 * 130 * 4 and n % 256 == 0
+    def r256(b):
+        return (b + 255) // 256 * 256
+    ws = pa.paged_attention_workspace_size
+    # single pass, or every sequence within one partition: nothing
+    assert ws(4, 8, 8, 128, 100, 0) == 0
+    assert ws(4, 8, 8, 128, 512, 512) == 0
+    # split-context: (max, sum, output) per (sequence, head, partition)
+    assert ws(4, 8, 8, 128, 1025, 512) == r256(4 * 8 * 3 * 130 * 4)
+    # balanced: two records of a unit's heads per worker, at most 32 workers
+    # per CU (16 when a KV head serves more than 16 query heads; MI355X: 256
+    # CUs, also the fallback without a device), then one 6-word range
+    # descriptor per worker (32 per CU); all per started window of 1024 sequences
+    cus = 256
+    for S, H, Hkv, D in ((4, 8, 2, 128), (4, 32, 32, 64), (1500, 71, 1, 64)):
+        windows = (S + 1023) // 1024
+        group = H // Hkv if H // Hkv >= 2 else 1
+        workers = cus * (16 if group > 16 else 32)
+        expect = r256(windows * workers * 2 * group * (D + 2) * 4) + \
+            r256(windows * cus * 32 * 6 * 8)
+        assert ws(S, H, Hkv, D, 100, -1) == expect
+    assert ws(0, 8, 8, 128, 100, 0) == 0
+    assert ws(4, 8, 8, 128, 100, -2) == 0
 
 
 def write_call(**kw):

@@ -35,7 +35,7 @@ def run_and_check(case, partitions=(0,), label=""):
     assert_pools_equal(dev, kp, vp)
     errs = {}
     for ps in partitions:
-        out = dev.attend(ps, out=torch.empty_like(dev.q))
+        out = dev.attend(ps, out=torch.full_like(dev.q, float("nan")))   # every element written
         torch.cuda.synchronize()
         errs[ps] = max_err(out_to_f64(out), ref, case.q_dtype)
         assert errs[ps] <= TOL[case.kv_dtype], (case.name, ps, errs[ps])
@@ -45,11 +45,11 @@ def run_and_check(case, partitions=(0,), label=""):
 
 # ------------------------------------------------------------------ the five workloads
 def test_tiny_fp32_config():
-    run_and_check(W.tiny_case(), partitions=(0, 4, 8, 12))
+    run_and_check(W.tiny_case(), partitions=(0, -1, 4, 8, 12))
 
 
 def test_opt13b_layer_fp16():
-    run_and_check(W.opt13b_case(), partitions=(0, 512, 128))
+    run_and_check(W.opt13b_case(), partitions=(0, -1, 512, 128))
 
 
 def test_llama7b_shape_reduced():
@@ -57,7 +57,7 @@ def test_llama7b_shape_reduced():
                               num_kv_heads=32, head_dim=128, block_size=16,
                               context_lens=[4096, 4096, 3001, 17, 1], kv_dtype="f16",
                               q_dtype="f16", spare_blocks=64)
-    run_and_check(case, partitions=(0, 512, 1024))
+    run_and_check(case, partitions=(0, -1, 512, 1024))
 
 
 @pytest.mark.parametrize("bs", [8, 16, 32, 64])
@@ -67,7 +67,7 @@ def test_falcon7b_mqa_fp8(bs):
                               num_kv_heads=1, head_dim=64, block_size=bs, context_lens=ctx,
                               kv_dtype="fp8_e4m3", q_dtype="f16",
                               num_blocks=W.falcon7b_num_blocks(ctx, bs))
-    run_and_check(case, partitions=(512, 0))
+    run_and_check(case, partitions=(512, 0, -1))
 
 
 def _llama70b(spec, num_blocks):
@@ -103,8 +103,8 @@ def test_llama70b_gqa_shared_prompt_cow(full):
     dev.write()
     torch.cuda.synchronize()
     assert_pools_equal(dev, kp, vp)
-    for ps in (0, 512):
-        out = dev.attend(ps, out=torch.empty_like(dev.q))
+    for ps in (0, 512, -1):
+        out = dev.attend(ps, out=torch.full_like(dev.q, float("nan")))
         torch.cuda.synchronize()
         err = max_err(out_to_f64(out), ref, "bf16")
         say(f"    partition {ps}: max-abs error {err:.3g}")
@@ -131,8 +131,8 @@ def test_llama7b_full_size_sampled():
     tables = torch.from_numpy(d["tables"]).cuda()
     ctx_t = torch.from_numpy(ctx).cuda()
     outs = {}
-    for ps in (0, 512):
-        out = torch.empty_like(d["q"])
+    for ps in (0, 512, -1):
+        out = torch.full_like(d["q"], float("nan"))
         pa.paged_attention_decode(out, d["q"], d["k_pool"], d["v_pool"], tables, ctx_t,
                                   max_context_len=4096, scale=d["scale"], partition_size=ps)
         torch.cuda.synchronize()
@@ -180,7 +180,7 @@ def test_edge_shapes(kv, q, D, bs, H, Hkv, ctx):
                               num_kv_heads=Hkv, head_dim=D, block_size=bs, context_lens=ctx,
                               kv_dtype=kv, q_dtype=q, spare_blocks=5, salt=bs + D,
                               max_blocks=int(W.blocks_needed(ctx, bs).max()) + 3)
-    run_and_check(case, partitions=(0, 3 * bs, 100))
+    run_and_check(case, partitions=(0, -1, 3 * bs, 100))
 
 
 def test_empty_batch_and_empty_contexts():
@@ -189,7 +189,7 @@ def test_empty_batch_and_empty_contexts():
                               q_dtype="f16", spare_blocks=2, append=False)
     dev = DeviceCase(case)
     say("[case] empty contexts")
-    for ps in (0, 16):
+    for ps in (0, 16, -1):
         out = dev.attend(ps, out=torch.full_like(dev.q, float("nan")))
         torch.cuda.synchronize()
         o = out_to_f64(out)
@@ -207,6 +207,7 @@ def test_placement_permutation_is_bit_identical():
     say("[case] placement permutation")
     a = DeviceCase(case).attend(0).clone()
     a_split = DeviceCase(case).attend(256).clone()
+    a_bal = DeviceCase(case).attend(-1).clone()
     perm = np.random.default_rng(1).permutation(case.num_blocks)
     k2 = np.empty_like(case.k_pool); v2 = np.empty_like(case.v_pool)
     k2[perm] = case.k_pool; v2[perm] = case.v_pool
@@ -215,9 +216,11 @@ def test_placement_permutation_is_bit_identical():
                                  -1).astype(np.int32)
     b = DeviceCase(case).attend(0)
     b_split = DeviceCase(case).attend(256)
+    b_bal = DeviceCase(case).attend(-1)
     torch.cuda.synchronize()
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
     assert torch.equal(a_split.view(torch.int16), b_split.view(torch.int16))
+    assert torch.equal(a_bal.view(torch.int16), b_bal.view(torch.int16))
 
 
 def test_invalid_table_entries_are_never_read():
@@ -355,7 +358,7 @@ def test_grouped_heads(kv, q, D, bs, H, Hkv, ctx):
                               num_heads=H, num_kv_heads=Hkv, head_dim=D, block_size=bs,
                               context_lens=ctx, kv_dtype=kv, q_dtype=q, spare_blocks=7,
                               salt=H * 7 + bs, max_blocks=int(W.blocks_needed(ctx, bs).max()) + 2)
-    run_and_check(case, partitions=(0, 64, 512))
+    run_and_check(case, partitions=(0, -1, 64, 512))
 
 
 def test_grouped_heads_invalid_table_entries():
@@ -375,3 +378,63 @@ def test_grouped_heads_invalid_table_entries():
         V = oracle.gather_sequence(case.v_pool, "bf16", good[s], n, 16)[keep]
         ref = oracle.contiguous_attention(Q[s], K, V, case.scale)
         assert max_err(out[s], ref, "bf16") <= TOL["bf16"]
+
+
+# ------------------------------------------------------------------ work sharing across launches
+WINDOW_CASES = [
+    # kv, q, H, Hkv (one case per decode kernel: per-head, grouped-head, large group)
+    ("f16", "f16", 4, 4),
+    ("bf16", "bf16", 8, 2),
+    ("fp8_e4m3", "f16", 32, 1),
+]
+
+
+@pytest.mark.parametrize("kv,q,H,Hkv", WINDOW_CASES)
+def test_many_windows_and_workspace_reuse(kv, q, H, Hkv):
+    """2500 sequences span three 1024-sequence windows of the schedule; one
+    workspace serves several eager launches and graph replays, which all agree
+    bit for bit."""
+    rng = np.random.default_rng(7)
+    ctx = rng.integers(0, 70, size=2500)
+    ctx[::97] = 0
+    ctx[5] = 400
+    case = W.make_decode_case(f"windows_{kv}_{H}_{Hkv}", "tiny", num_seqs=len(ctx), num_heads=H,
+                              num_kv_heads=Hkv, head_dim=64, block_size=16,
+                              context_lens=ctx.tolist(), kv_dtype=kv, q_dtype=q, spare_blocks=7,
+                              append=False)
+    dev = DeviceCase(case)
+    say(f"[case] windows kv={kv} q={q} H={H} Hkv={Hkv}")
+    ref = oracle.paged_attention(case.q, q, case.k_pool, case.v_pool, kv, case.block_tables,
+                                 case.context_lens, 16, case.scale, case.k_scale, case.v_scale)
+    for ps in (0, 32, pa.PARTITION_BALANCED):
+        need = pa.paged_attention_workspace_size(len(ctx), H, Hkv, 64, case.max_context_len, ps)
+        ws = pa.new_workspace(need, "cuda")
+        outs = []
+
+        def launch(out):
+            pa.paged_attention_decode(out, dev.q, dev.k_pool, dev.v_pool, dev.tables, dev.ctx,
+                                      max_context_len=case.max_context_len, scale=case.scale,
+                                      k_scale=case.k_scale, v_scale=case.v_scale,
+                                      partition_size=ps, workspace=ws)
+
+        for _ in range(3):
+            out = torch.full_like(dev.q, float("nan"))
+            launch(out)
+            torch.cuda.synchronize()
+            outs.append(out_to_f64(out))
+        g_out = torch.full_like(dev.q, float("nan"))
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            launch(g_out)
+        for rep in range(3):
+            g_out.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            outs.append(out_to_f64(g_out))
+        for i, o in enumerate(outs):
+            err = max_err(o, ref, q)
+            say(f"    partition {ps} launch {i}: max-abs error {err:.3g}")
+            assert err <= TOL[kv]
+            assert np.array_equal(o, outs[0]), "launches differ"
+        del g
