@@ -286,6 +286,11 @@ class Tiny(HostLayers):
         self.finish(pa, torch, partition_size, self.ctx.max())
 
 
+# launch configuration per workload: the fastest measured on MI355X (uniform
+# long contexts: one pass per (sequence, head); ragged batches: balanced split;
+# the large-group kernel: 512-token partitions)
+DEFAULT_PARTITION = {"llama7b": 0, "opt13b": -1, "falcon7b": 512, "llama70b": -1, "tiny": 0}
+
 WORKLOADS = {"llama7b": Llama7B, "opt13b": Opt13B, "falcon7b": Falcon7B, "llama70b": Llama70B,
              "tiny": Tiny}
 
@@ -302,7 +307,8 @@ def read_traffic(workload, partition_size):
             if line and not line.startswith("#") and "=" in line:
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-        if kv.get("workload") != workload or int(kv.get("partition_size", -1)) != partition_size:
+        if kv.get("workload") != workload or "partition_size" not in kv or \
+                int(kv["partition_size"]) != partition_size:
             continue
         h = hashlib.sha256()
         for src in kv["sources"].split():
@@ -333,7 +339,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama7b", choices=sorted(WORKLOADS))
-    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="0 single pass, > 0 split-context partitions, -1 balanced split "
+                         "(default: the fastest measured for the workload)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="budget of the CPU-oracle baseline sample (0 = skip)")
     ap.add_argument("--decode-iters", type=int, default=64)
@@ -360,6 +368,8 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy_mib > 0:
         calibrate_copy(pa, torch, args.calibrate_copy_mib)
+    if args.partition_size is None:
+        args.partition_size = DEFAULT_PARTITION[args.workload]
     wl = WORKLOADS[args.workload](pa, W, torch, args.partition_size, args)
 
     # one step and one round of decode launches (every layer once), eager or as HIP graphs
