@@ -61,7 +61,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
     Schedule<NT> sch;
     for (int s0 = 0; s0 < a.num_seqs; s0 += kWindow) {
         sch.build(a, s0, min(kWindow, a.num_seqs - s0), a.num_heads, wl_lds,
-                  blockIdx.x * NW + wave, gridDim.x * NW, lane == 0);
+                  worker_id(wave, NW), gridDim.x * NW, lane == 0);
         Item itm;
         while (sch.next(a, itm)) {
             const int s = itm.s;
@@ -270,32 +270,78 @@ __global__ __launch_bounds__(64) void lse_reduce_kernel(DecodeArgs a) {
 // past their end holds the last piece; its descriptor names the segment, and
 // the pieces are held by workers first..b (first: slot 1 unless its range
 // starts exactly at the segment, every other one: slot 0).  One wavefront per
-// (worker, head of a unit); most find that their worker ends no cut segment.
+// worker: it reads the worker's descriptor and, if the worker holds such a
+// last piece, merges all heads of the segment's unit, kSplitHeads heads per
+// pass with 16 consecutive dimensions of one head per lane (so every record
+// is fetched in 16-byte pieces, all records of a batch at once).
 template <int QDT, int D>
-__global__ __launch_bounds__(1024) void split_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void split_reduce_kernel(DecodeArgs a) {
+    constexpr int LPH = D / 16;                 // lanes per head
+    constexpr int HP = 64 / LPH;                // heads per pass
+    constexpr int B = 8;                        // records per batch
     const int64_t windows = (a.num_seqs + kWindow - 1) / kWindow;
     const int G = a.num_heads / a.units;
-    const int64_t total = windows * a.workers * G;
-    const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
-    for (int64_t x = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); x < total;
-         x += waves) {
-        const int64_t wb = x / G;
-        const int i = (int)(x % G);
-        const int64_t* d = a.desc + wb * kDescWords;
-        const int64_t t0 = d[1], range = d[3];
-        const int64_t run = split_run((int)d[4]);
-        const int64_t win = wb / a.workers, b = wb % a.workers;
-        if (t0 <= 0 || t0 >= run) continue;             // no cut tokens end in this range
-        const int64_t start = b * range - t0;           // the segment's first token, range space
-        if (start + run > (b + 1) * range) continue;    // a later range holds the last piece
-        const int64_t first = start / range;
-        const int s = (int)(d[0] & 0xFFFFFFFF), unit = (int)(d[0] >> 32);
+    const int lane = threadIdx.x & 63;
+    const int hl = lane / LPH, d0 = (lane % LPH) * 16;
+    const int64_t wb = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (wb >= windows * a.workers) return;
+    const int64_t* d = a.desc + wb * kDescWords;
+    const int64_t t0 = d[1], range = d[3];
+    const int64_t run = split_run((int)d[4]);
+    const int64_t win = wb / a.workers, b = wb % a.workers;
+    if (t0 <= 0 || t0 >= run) return;                   // no cut tokens end in this range
+    const int64_t start = b * range - t0;               // the segment's first token, range space
+    if (start + run > (b + 1) * range) return;          // a later range holds the last piece
+    const int64_t first = start / range;
+    const int n = (int)(b - first + 1);
+    const int s = (int)(d[0] & 0xFFFFFFFF), unit = (int)(d[0] >> 32);
+    for (int h0 = 0; h0 < G; h0 += HP) {
+        const int i = min(h0 + hl, G - 1);              // lanes past the group repeat its last head
         auto rec = [&](int k) -> int64_t {
             const int64_t w = first + k;
             return ((win * a.workers + w) * 2 + (w * range >= start ? 0 : 1)) * G + i;
         };
-        merge_records<QDT, D>(a, (int)(b - first + 1), rec,
-                              (int64_t)s * a.num_heads + (int64_t)unit * G + i);
+        float M = kNegInf, den = 0.0f, num[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) num[e] = 0.0f;
+        for (int k0 = 0; k0 < n; k0 += B) {
+            float mv[B], lv[B];
+            float4 ov[B][4];
+#pragma unroll
+            for (int q = 0; q < B; ++q) {
+                const int64_t r = rec(min(k0 + q, n - 1));
+                mv[q] = a.ws[r];
+                lv[q] = a.ws[a.nrec + r];
+                const float4* op = reinterpret_cast<const float4*>(a.ws + 2 * a.nrec + r * D + d0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) ov[q][v] = op[v];
+            }
+#pragma unroll
+            for (int q = 0; q < B; ++q) {
+                if (k0 + q < n && mv[q] != kNegInf) {
+                    const float Mn = fmaxf(M, mv[q]);
+                    const float sc = (M == kNegInf) ? 0.0f : fast_exp2(M - Mn);
+                    const float w = fast_exp2(mv[q] - Mn) * lv[q];
+                    den = den * sc + w;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        num[4 * v + 0] = num[4 * v + 0] * sc + w * ov[q][v].x;
+                        num[4 * v + 1] = num[4 * v + 1] * sc + w * ov[q][v].y;
+                        num[4 * v + 2] = num[4 * v + 2] * sc + w * ov[q][v].z;
+                        num[4 * v + 3] = num[4 * v + 3] * sc + w * ov[q][v].w;
+                    }
+                    M = Mn;
+                }
+            }
+        }
+        if (h0 + hl < G) {
+            const float f = den > 0.0f ? a.out_scale / den : 0.0f;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) num[e] *= f;
+            char* op = reinterpret_cast<char*>(a.out) +
+                       (((int64_t)s * a.num_heads + (int64_t)unit * G + i) * D + d0) * elem_bytes(QDT);
+            store_vals<QDT>(op, num, 16);
+        }
     }
 }
 
@@ -337,13 +383,9 @@ hipError_t launch_valu(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
 template <int QDT>
 hipError_t launch_reduce(DecodeArgs& a, int head_dim, hipStream_t stream) {
     if (a.part_tokens < 0) {
-        const int64_t waves = (a.num_seqs + kWindow - 1) / kWindow * (int64_t)a.workers *
-                              (a.num_heads / a.units);
+        const int64_t waves = (a.num_seqs + kWindow - 1) / kWindow * (int64_t)a.workers;
         auto k = head_dim == 64 ? split_reduce_kernel<QDT, 64> : split_reduce_kernel<QDT, 128>;
-        // large workgroups: most wavefronts only read one descriptor, and
-        // dispatching many small workgroups would cost more than their work
-        const int64_t grid = persistent_grid(reinterpret_cast<const void*>(k), 1024, (waves + 15) / 16);
-        hipLaunchKernelGGL(k, dim3((uint32_t)grid), dim3(1024), 0, stream, a);
+        hipLaunchKernelGGL(k, dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0, stream, a);
         return hipGetLastError();
     }
     const int64_t pairs = (int64_t)a.num_seqs * a.num_heads;

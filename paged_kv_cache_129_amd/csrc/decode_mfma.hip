@@ -129,7 +129,7 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     Schedule<NT> sch;
     for (int s0 = 0; s0 < a.num_seqs; s0 += kWindow) {
         sch.build(a, s0, min(kWindow, a.num_seqs - s0), a.num_kv_heads, wl_lds,
-                  blockIdx.x * NW + wave, gridDim.x * NW, lane == 0);
+                  worker_id(wave, NW), gridDim.x * NW, lane == 0);
         Item itm;
         while (sch.next(a, itm)) {
             const int s = itm.s;

@@ -5,7 +5,10 @@
 // with all the query heads of its group (grouped kernels).  Items are taken by
 // "workers": single wavefronts in the per-head and grouped kernels (each
 // streams its own items, so one wavefront's wait for memory never idles its
-// neighbours), whole workgroups in the large-group kernel.  Launches are
+// neighbours), whole workgroups in the large-group kernel.  Wavefront w of
+// workgroup b is worker b * NW + w (measured: spreading consecutive workers
+// over workgroups instead is no faster for ragged batches and slower for
+// uniform ones).  Launches are
 // persistent: the grid is what the GPU holds at once, and the workers walk the
 // live work only, since on this chip every dispatched workgroup costs time
 // even when it has nothing to do.  Sequences are taken in windows of kWindow,
@@ -124,6 +127,9 @@ __device__ __forceinline__ int64_t uni(int64_t x) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
+
+// worker index of wavefront `wave` of this workgroup (NW wavefronts each)
+__device__ __forceinline__ int worker_id(int wave, int nw) { return (int)blockIdx.x * nw + wave; }
 
 // One work item: tokens [t0, t1) of unit `unit` of sequence `s`, of a context
 // of `ctx` tokens.  `whole`: the item is the entire context and its result is
