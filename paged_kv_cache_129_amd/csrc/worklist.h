@@ -8,10 +8,9 @@
 // neighbours), whole workgroups in the large-group kernel.  Wavefront w of
 // workgroup b is worker b * NW + w (measured: spreading consecutive workers
 // over workgroups instead is no faster for ragged batches and slower for
-// uniform ones).  Launches are
-// persistent: the grid is what the GPU holds at once, and the workers walk the
-// live work only, since on this chip every dispatched workgroup costs time
-// even when it has nothing to do.  Sequences are taken in windows of kWindow,
+// uniform ones).  Launches are persistent: the grid is what the GPU holds at
+// once, and the workers walk the live work only, since on this chip every
+// dispatched workgroup costs time even when it has nothing to do.  Sequences are taken in windows of kWindow,
 // whose metadata every workgroup stages in LDS.  Two schedules:
 //
 // * Partitions (partition_size >= 0): a segment is cut into partitions of
