@@ -311,9 +311,12 @@ def read_traffic(workload, partition_size):
                 int(kv["partition_size"]) != partition_size:
             continue
         h = hashlib.sha256()
-        for src in kv["sources"].split():
-            with open(os.path.join(ROOT, src), "rb") as f:
-                h.update(f.read())
+        try:
+            for src in kv["sources"].split():
+                with open(os.path.join(ROOT, src), "rb") as f:
+                    h.update(f.read())
+        except OSError:                 # a source of the profiled build is gone
+            continue
         if h.hexdigest() == kv["source_sha256"]:
             return int(float(kv["traffic_bytes"])), os.path.basename(path)
     return None, None

@@ -59,23 +59,24 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 // Balanced split: partial records for two slots per (window, worker) and the
 // workers' range descriptors, for the most workers a launch can have on the
 // current device.
-size_t balanced_record_bytes(int64_t num_seqs, int64_t group, int64_t head_dim) {
+size_t balanced_record_bytes(int64_t num_seqs, int64_t unit_heads, int64_t head_dim) {
     const int64_t windows = (num_seqs + pa::kWindow - 1) / pa::kWindow;
-    const int64_t workers = (int64_t)pa::device_cus() * pa::balanced_workers_per_cu((int)group);
-    return round256((size_t)(windows * workers * 2 * group) * (size_t)(head_dim + 2) * sizeof(float));
+    const int64_t workers = (int64_t)pa::device_cus() * pa::kMaxWorkersPerCu;
+    return round256((size_t)(windows * workers * 2 * unit_heads) * (size_t)(head_dim + 2) * sizeof(float));
 }
 size_t balanced_desc_bytes(int64_t num_seqs) {
     const int64_t windows = (num_seqs + pa::kWindow - 1) / pa::kWindow;
-    const int64_t workers = (int64_t)pa::device_cus() * pa::balanced_workers_per_cu(1);
+    const int64_t workers = (int64_t)pa::device_cus() * pa::kMaxWorkersPerCu;
     return round256((size_t)(windows * workers) * pa::kDescWords * sizeof(int64_t));
 }
 
-// group of query heads one work unit covers: all of a KV head's query heads
-// for the grouped kernels, one head for the per-head kernel
-int64_t unit_group(int32_t num_heads, int32_t num_kv_heads) {
-    return num_kv_heads > 0 && num_heads % num_kv_heads == 0 && num_heads / num_kv_heads >= 2
-               ? num_heads / num_kv_heads
-               : 1;
+// record slots per work unit: the matrix-core kernel's unit heads when it may
+// run (2 <= G <= kMaxGroup), else one head (per-head kernel); an upper bound
+// whichever kernel the data types select
+int64_t unit_group(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim) {
+    if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return 1;
+    const int g = num_heads / num_kv_heads;
+    return g >= 2 && g <= pa::kMaxGroup ? pa::mfma_unit_heads(g, head_dim) : 1;
 }
 
 }  // namespace
@@ -151,7 +152,7 @@ size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, in
         max_context_len < 0 || (partition_size < 0 && partition_size != PA_PARTITION_BALANCED))
         return 0;
     if (partition_size == PA_PARTITION_BALANCED)
-        return balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads), head_dim) +
+        return balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads, head_dim), head_dim) +
                balanced_desc_bytes(num_seqs);
     return partial_bytes(num_seqs, num_heads, head_dim,
                          num_partitions(max_context_len, partition_size));
@@ -193,7 +194,7 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
     const int64_t parts = balanced ? 1 : num_partitions(ctx_cap, partition_size);
     if ((int64_t)num_seqs * num_heads * parts >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
     const size_t rec_bytes =
-        balanced ? balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads), head_dim)
+        balanced ? balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads, head_dim), head_dim)
                  : partial_bytes(num_seqs, num_heads, head_dim, parts);
     const size_t need =
         rec_bytes + (balanced ? balanced_desc_bytes(num_seqs) : 0);

@@ -280,7 +280,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(DecodeArgs a) {
     constexpr int HP = 64 / LPH;                // heads per pass
     constexpr int B = 8;                        // records per batch
     const int64_t windows = (a.num_seqs + kWindow - 1) / kWindow;
-    const int G = a.num_heads / a.units;
+    const int GR = a.unit_heads;                        // record slots per unit
     const int lane = threadIdx.x & 63;
     const int hl = lane / LPH, d0 = (lane % LPH) * 16;
     const int64_t wb = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
@@ -295,11 +295,15 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(DecodeArgs a) {
     const int64_t first = start / range;
     const int n = (int)(b - first + 1);
     const int s = (int)(d[0] & 0xFFFFFFFF), unit = (int)(d[0] >> 32);
-    for (int h0 = 0; h0 < G; h0 += HP) {
-        const int i = min(h0 + hl, G - 1);              // lanes past the group repeat its last head
+    const int Gq = a.num_heads / a.num_kv_heads;
+    const int hg0 = (unit % a.units_per_kv) * GR;
+    const int nh = min(GR, Gq - hg0);                   // heads of the unit
+    const int64_t head0 = (int64_t)(unit / a.units_per_kv) * Gq + hg0;
+    for (int h0 = 0; h0 < nh; h0 += HP) {
+        const int i = min(h0 + hl, nh - 1);             // lanes past the unit repeat its last head
         auto rec = [&](int k) -> int64_t {
             const int64_t w = first + k;
-            return ((win * a.workers + w) * 2 + (w * range >= start ? 0 : 1)) * G + i;
+            return ((win * a.workers + w) * 2 + (w * range >= start ? 0 : 1)) * GR + i;
         };
         float M = kNegInf, den = 0.0f, num[16];
 #pragma unroll
@@ -334,12 +338,12 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(DecodeArgs a) {
                 }
             }
         }
-        if (h0 + hl < G) {
+        if (h0 + hl < nh) {
             const float f = den > 0.0f ? a.out_scale / den : 0.0f;
 #pragma unroll
             for (int e = 0; e < 16; ++e) num[e] *= f;
             char* op = reinterpret_cast<char*>(a.out) +
-                       (((int64_t)s * a.num_heads + (int64_t)unit * G + i) * D + d0) * elem_bytes(QDT);
+                       (((int64_t)s * a.num_heads + head0 + i) * D + d0) * elem_bytes(QDT);
             store_vals<QDT>(op, num, 16);
         }
     }
@@ -350,6 +354,8 @@ hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
     constexpr int NW = 4;
     constexpr int U = 4;
     auto kernel = decode_valu_kernel<KVDT, QDT, D, NW, U>;
+    a.unit_heads = 1;                                   // a unit is one query head
+    a.units_per_kv = a.num_heads / a.num_kv_heads;
     const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), NW * 64, a.num_heads, 1, a);
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
@@ -454,10 +460,9 @@ int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers
     const int per_wg = wave_workers ? threads / 64 : 1;
     int64_t grid;
     if (a.part_tokens < 0) {
-        const int64_t cap = (int64_t)device_cus() * balanced_workers_per_cu(a.num_heads / units) / per_wg;
-        grid = persistent_grid(kernel, threads, cap);
+        grid = persistent_grid(kernel, threads, (int64_t)device_cus() * kMaxWorkersPerCu / per_wg);
         const int64_t windows = (a.num_seqs + kWindow - 1) / kWindow;
-        a.nrec = windows * grid * per_wg * 2 * (a.num_heads / units);
+        a.nrec = windows * grid * per_wg * 2 * a.unit_heads;
     } else {
         grid = persistent_grid(kernel, threads, ((int64_t)a.num_seqs * units * a.num_parts + per_wg - 1) / per_wg);
     }
@@ -471,8 +476,6 @@ hipError_t launch_decode(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
     hipError_t e;
     if (decode_mfma_supported(q_dt, kv_dt, head_dim, group))
         e = launch_decode_mfma(a, q_dt, kv_dt, head_dim, stream);
-    else if (decode_mqa_supported(q_dt, kv_dt, head_dim, group))
-        e = launch_decode_mqa(a, q_dt, kv_dt, head_dim, stream);
     else
         e = launch_valu(a, q_dt, kv_dt, head_dim, stream);
     if (e != hipSuccess || (a.part_tokens >= 0 && a.num_parts <= 1)) return e;

@@ -95,11 +95,11 @@ __device__ __forceinline__ int dmap(int c, int j) {
     return 32 * c + 8 * j;
 }
 
-template <int KVDT, int QDT, int D, int NW>
+template <int KVDT, int QDT, int D, int NW, int TILES>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = (KVDT == PA_FP8_E4M3) ? PA_F16 : KVDT;   // MFMA operand type
     constexpr int EB = elem_bytes(KVDT);
-    constexpr int NC = D / 32;               // score MFMAs per chunk
+    constexpr int NC = D / 32;               // score MFMAs per chunk and tile
     constexpr int NDT = D / 16;              // output d-tiles
     constexpr int LDV = D + 8;               // LDS row stride of a staged V tile (halfs)
     constexpr int PPR = D * EB / 16;         // 16-byte pieces per V row
@@ -128,24 +128,29 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 
     Schedule<NT> sch;
     for (int s0 = 0; s0 < a.num_seqs; s0 += kWindow) {
-        sch.build(a, s0, min(kWindow, a.num_seqs - s0), a.num_kv_heads, wl_lds,
-                  worker_id(wave, NW), gridDim.x * NW, lane == 0);
+        sch.build(a, s0, min(kWindow, a.num_seqs - s0), a.units, wl_lds, worker_id(wave, NW),
+                  gridDim.x * NW, lane == 0);
         Item itm;
         while (sch.next(a, itm)) {
             const int s = itm.s;
-            const int kvh = itm.unit;
+            const int kvh = itm.unit / a.units_per_kv;
+            const int hg0 = (itm.unit % a.units_per_kv) * a.unit_heads;   // first head of the unit, within the group
+            const int nh = min(a.unit_heads, G - hg0);                   // heads of the unit
             // first loads of the item, issued together: block-table segment, query
             const int t0 = itm.t0, t1 = itm.t1;
             const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
             TablePrefetch<64, WT> tpre;
             tpre.issue(trow, t0 >> a.log2_bs, table_span(a, t0, t1, WT), a.max_blocks, lane);
 
-            // B operand of the score MFMA: Q^T[d][head], head = c16 (zero for padding heads)
-            Op8 qop[NC];
-            {
-                const bool live = c16 < G;
+            // B operands of the score MFMA: Q^T[d][head] per 16-head tile, head = 16 tt + c16
+            // of the unit (zero for padding heads)
+            Op8 qop[TILES][NC];
+#pragma unroll
+            for (int tt = 0; tt < TILES; ++tt) {
+                const int hu = 16 * tt + c16;
+                const bool live = hu < nh;
                 const char* qrow = reinterpret_cast<const char*>(a.q) +
-                                   ((int64_t)s * a.num_heads + kvh * G + (live ? c16 : 0)) * D *
+                                   ((int64_t)s * a.num_heads + kvh * G + hg0 + (live ? hu : 0)) * D *
                                        elem_bytes(QDT);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
@@ -161,17 +166,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                         for (int q = 0; q < 4; ++q) o.w[q] = live ? pack_f16(f[2 * q], f[2 * q + 1]) : 0u;
                     }
-                    qop[c] = o;
+                    qop[tt][c] = o;
                 }
             }
             // settle the one-time loads here: the wait-count analysis cannot see across
             // the token loop's back edge that they completed
             __builtin_amdgcn_s_waitcnt(0);
 
-            float m = kNegInf, l = 0.0f;
-            f32x4 acc[NDT];
+            float m[TILES], l[TILES];
+            f32x4 acc[TILES][NDT];
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int tt = 0; tt < TILES; ++tt) {
+                m[tt] = kNegInf;
+                l[tt] = 0.0f;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 
             const int b_first = t0 >> a.log2_bs;
             const int b_end = (t1 + bs - 1) >> a.log2_bs;
@@ -248,49 +258,53 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                             kop[c] = R.k[c];
                         }
                     }
-                    // ---- scores S^T[token][head]
-                    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int c = 0; c < NC; ++c) sc = mma32<MT>(kop[c], qop[c], sc);
-
-                    // ---- online softmax per head column
-                    float sv[4];
                     bool live[4];
-                    float mx = kNegInf;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        live[i] = row_of(c0 + 4 * j + i) >= 0;
-                        sv[i] = live[i] ? sc[i] * a.qk_scale : kNegInf;
-                        mx = fmaxf(mx, sv[i]);
-                    }
-                    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                    const float mn = fmaxf(m, mx);
-                    const float alpha = (m == kNegInf) ? 0.0f : fast_exp2(m - mn);
-                    float pr[4];
-                    float psum = 0.0f;
+                    for (int i = 0; i < 4; ++i) live[i] = row_of(c0 + 4 * j + i) >= 0;
+
+                    // ---- per tile: scores S^T[token][head], online softmax per head column
+                    Op4 pop[TILES], plo[TILES];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        pr[i] = live[i] ? fast_exp2(sv[i] - mn) : 0.0f;
-                        psum += pr[i];
-                    }
-                    l = l * alpha + psum;
-                    m = mn;
+                    for (int tt = 0; tt < TILES; ++tt) {
+                        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-                    Op4 pop, plo;
-                    pop.w[0] = pack2<MT>(pr[0], pr[1]);
-                    pop.w[1] = pack2<MT>(pr[2], pr[3]);
-                    if constexpr (MT == PA_BF16) {
+                        for (int c = 0; c < NC; ++c) sc = mma32<MT>(kop[c], qop[tt][c], sc);
+                        float sv[4];
+                        float mx = kNegInf;
 #pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            const float h0 = __uint_as_float(pop.w[q] << 16);
-                            const float h1 = __uint_as_float(pop.w[q] & 0xFFFF0000u);
-                            plo.w[q] = pack2<MT>(pr[2 * q] - h0, pr[2 * q + 1] - h1);
+                        for (int i = 0; i < 4; ++i) {
+                            sv[i] = live[i] ? sc[i] * a.qk_scale : kNegInf;
+                            mx = fmaxf(mx, sv[i]);
+                        }
+                        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+                        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+                        const float mn = fmaxf(m[tt], mx);
+                        const float alpha = (m[tt] == kNegInf) ? 0.0f : fast_exp2(m[tt] - mn);
+                        float pr[4];
+                        float psum = 0.0f;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            pr[i] = live[i] ? fast_exp2(sv[i] - mn) : 0.0f;
+                            psum += pr[i];
+                        }
+                        l[tt] = l[tt] * alpha + psum;
+                        m[tt] = mn;
+#pragma unroll
+                        for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] *= alpha;
+                        pop[tt].w[0] = pack2<MT>(pr[0], pr[1]);
+                        pop[tt].w[1] = pack2<MT>(pr[2], pr[3]);
+                        if constexpr (MT == PA_BF16) {
+#pragma unroll
+                            for (int q = 0; q < 2; ++q) {
+                                const float h0 = __uint_as_float(pop[tt].w[q] << 16);
+                                const float h1 = __uint_as_float(pop[tt].w[q] & 0xFFFF0000u);
+                                plo[tt].w[q] = pack2<MT>(pr[2 * q] - h0, pr[2 * q + 1] - h1);
+                            }
                         }
                     }
 
-                    // ---- stage V rows (zero for absent tokens), read back transposed
+                    // ---- stage V rows (zero for absent tokens), read back transposed,
+                    // each V^T operand serving every tile
 #pragma unroll
                     for (int u = 0; u < NPV; ++u) {
                         const int p = u * 64 + lane;
@@ -317,8 +331,11 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                         Op4 vop;
                         vop.w[0] = (uint32_t)col[0] | ((uint32_t)col[LDV] << 16);
                         vop.w[1] = (uint32_t)col[2 * LDV] | ((uint32_t)col[3 * LDV] << 16);
-                        acc[dt] = mma16<MT>(vop, pop, acc[dt]);
-                        if constexpr (MT == PA_BF16) acc[dt] = mma16<MT>(vop, plo, acc[dt]);
+#pragma unroll
+                        for (int tt = 0; tt < TILES; ++tt) {
+                            acc[tt][dt] = mma16<MT>(vop, pop[tt], acc[tt][dt]);
+                            if constexpr (MT == PA_BF16) acc[tt][dt] = mma16<MT>(vop, plo[tt], acc[tt][dt]);
+                        }
                     }
                     __builtin_amdgcn_wave_barrier();
                 };
@@ -337,30 +354,35 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
             }
 
             // ---- per-column totals, then this wavefront's result for its item
-            l += __shfl_xor(l, 16, 64);
-            l += __shfl_xor(l, 32, 64);
-            if (c16 < G) {
-                const int head = kvh * G + c16;
-                const float inv_l = l > 0.0f ? 1.0f / l : 0.0f;
-                const int64_t r = itm.rec0 + (int64_t)c16 * itm.rec_stride;
-                if (!itm.whole && j == 0) {
-                    a.ws[r] = m;
-                    a.ws[a.nrec + r] = l;
-                }
 #pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) {
-                    const int d = 16 * dt + 4 * j;
-                    if (itm.whole) {
-                        const float f = inv_l * a.out_scale;
-                        char* op = reinterpret_cast<char*>(a.out) +
-                                   (((int64_t)s * a.num_heads + head) * D + d) * elem_bytes(QDT);
-                        *reinterpret_cast<uint2*>(op) =
-                            make_uint2(pack2<QDT>(acc[dt][0] * f, acc[dt][1] * f),
-                                       pack2<QDT>(acc[dt][2] * f, acc[dt][3] * f));
-                    } else {
-                        float* wo = a.ws + 2 * a.nrec + r * D + d;
+            for (int tt = 0; tt < TILES; ++tt) {
+                float lt = l[tt];
+                lt += __shfl_xor(lt, 16, 64);
+                lt += __shfl_xor(lt, 32, 64);
+                const int hu = 16 * tt + c16;
+                if (hu < nh) {
+                    const int head = kvh * G + hg0 + hu;
+                    const float inv_l = lt > 0.0f ? 1.0f / lt : 0.0f;
+                    const int64_t r = itm.rec0 + (int64_t)hu * itm.rec_stride;
+                    if (!itm.whole && j == 0) {
+                        a.ws[r] = m[tt];
+                        a.ws[a.nrec + r] = lt;
+                    }
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) wo[i] = acc[dt][i] * inv_l;
+                    for (int dt = 0; dt < NDT; ++dt) {
+                        const int d = 16 * dt + 4 * j;
+                        if (itm.whole) {
+                            const float f = inv_l * a.out_scale;
+                            char* op = reinterpret_cast<char*>(a.out) +
+                                       (((int64_t)s * a.num_heads + head) * D + d) * elem_bytes(QDT);
+                            *reinterpret_cast<uint2*>(op) =
+                                make_uint2(pack2<QDT>(acc[tt][dt][0] * f, acc[tt][dt][1] * f),
+                                           pack2<QDT>(acc[tt][dt][2] * f, acc[tt][dt][3] * f));
+                        } else {
+                            float* wo = a.ws + 2 * a.nrec + r * D + d;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) wo[i] = acc[tt][dt][i] * inv_l;
+                        }
                     }
                 }
             }
@@ -368,13 +390,33 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     }
 }
 
-template <int KVDT, int QDT, int D>
-hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
+template <int KVDT, int QDT, int D, int TILES>
+hipError_t launch_tiles(DecodeArgs& a, hipStream_t stream) {
     constexpr int NW = 4;
-    auto kernel = decode_mfma_kernel<KVDT, QDT, D, NW>;
-    const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), NW * 64, a.num_kv_heads, 1, a);
+    auto kernel = decode_mfma_kernel<KVDT, QDT, D, NW, TILES>;
+    const int G = a.num_heads / a.num_kv_heads;
+    a.unit_heads = G <= 16 ? G : 16 * TILES;
+    a.units_per_kv = (G + a.unit_heads - 1) / a.unit_heads;
+    const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), NW * 64,
+                                     a.num_kv_heads * a.units_per_kv, 1, a);
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int KVDT, int QDT, int D>
+hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
+    switch (mfma_tiles(a.num_heads / a.num_kv_heads, D)) {
+        case 1: return launch_tiles<KVDT, QDT, D, 1>(a, stream);
+        case 2: return launch_tiles<KVDT, QDT, D, 2>(a, stream);
+    }
+    if constexpr (D == 64) {
+        switch (mfma_tiles(a.num_heads / a.num_kv_heads, D)) {
+            case 3: return launch_tiles<KVDT, QDT, D, 3>(a, stream);
+            case 4: return launch_tiles<KVDT, QDT, D, 4>(a, stream);
+            case 5: return launch_tiles<KVDT, QDT, D, 5>(a, stream);
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int KVDT, int QDT>
@@ -387,7 +429,7 @@ hipError_t launch_dim(DecodeArgs& a, int head_dim, hipStream_t stream) {
 }  // namespace
 
 bool decode_mfma_supported(int q_dt, int kv_dt, int head_dim, int group) {
-    if (group < 2 || group > 16) return false;
+    if (group < 2 || group > kMaxGroup) return false;
     if (head_dim != 64 && head_dim != 128) return false;
     if (q_dt != PA_F16 && q_dt != PA_BF16) return false;
     return kv_dt == q_dt || kv_dt == PA_FP8_E4M3;

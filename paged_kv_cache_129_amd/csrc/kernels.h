@@ -37,15 +37,29 @@ struct CopyArgs {
 hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
 
 // Sequences are scheduled in windows of kWindow (their metadata is staged in
-// LDS).  The balanced schedule gives each worker (a wavefront or a workgroup)
-// two partial-record slots and one range descriptor per window; a launch has
-// at most balanced_workers_per_cu(group) workers per CU, so that the workspace
-// can be sized before the kernel is chosen.
+// LDS).  The balanced schedule gives each worker (a wavefront) two
+// partial-record slots and one range descriptor per window; a launch has at
+// most kMaxWorkersPerCu workers per CU, so that the workspace can be sized
+// before the launch.
 constexpr int kWindow = 1024;
 constexpr int kDescWords = 6;
-// 32 wavefronts per CU at most; the large-group kernel's workers are
-// workgroups of at least two wavefronts
-__host__ __device__ constexpr int balanced_workers_per_cu(int group) { return group > 16 ? 16 : 32; }
+// 32 wavefronts per CU at most, each a worker
+constexpr int kMaxWorkersPerCu = 32;
+
+// Matrix-core kernel: a wavefront computes up to 5 (head_dim 64) or 2 (head_dim
+// 128) 16-head tiles of one KV head's query heads from one read of K and V;
+// larger groups are split into units of equal tile counts.
+constexpr int kMaxGroup = 128;
+__host__ __device__ constexpr int mfma_tiles(int group, int head_dim) {
+    const int tiles = (group + 15) / 16;
+    const int tmax = head_dim == 64 ? 5 : 2;
+    const int units = (tiles + tmax - 1) / tmax;
+    return (tiles + units - 1) / units;
+}
+// query heads per work unit (record slots per unit) of the matrix-core kernel
+__host__ __device__ constexpr int mfma_unit_heads(int group, int head_dim) {
+    return group <= 16 ? group : 16 * mfma_tiles(group, head_dim);
+}
 
 struct DecodeArgs {
     const void* q;
@@ -57,7 +71,11 @@ struct DecodeArgs {
     float* ws;                  // partial records: m[nrec], l[nrec], o[nrec][head_dim]
     int64_t nrec;               // partial records in ws (set with the grid when balanced)
     int64_t* desc;              // balanced: 4 words per (window, workgroup) for the reduction
-    int32_t units;              // work units per sequence: query heads or KV heads (set at launch)
+    int32_t units;              // work units per sequence (set at launch): a unit is
+                                // unit_heads query heads of KV head unit / units_per_kv,
+                                // from head (unit % units_per_kv) * unit_heads of its group
+    int32_t units_per_kv;
+    int32_t unit_heads;
     int32_t workers;            // workers of the attention launch (set at launch)
     int32_t num_seqs;
     int32_t num_heads;
@@ -75,21 +93,19 @@ struct DecodeArgs {
 
 // compute units of the current device (cached per device)
 int device_cus();
-// Grid of an attention launch with `units` work units per sequence, whose
-// workers are wavefronts (wave_workers) or workgroups; records the worker
-// count (and, when balanced, the partial-record count) in `a`.
+// Grid of an attention launch with `units` work units per sequence (unit_heads
+// and units_per_kv already set), whose workers are wavefronts (wave_workers) or
+// workgroups; records the worker count (and, when balanced, the partial-record
+// count) in `a`.
 int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers, DecodeArgs& a);
 hipError_t launch_decode(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                          hipStream_t stream);
 
-// matrix-core kernel for grouped heads (decode_mfma.hip)
+// matrix-core kernel for grouped heads, 2 <= G <= kMaxGroup (decode_mfma.hip)
 bool decode_mfma_supported(int q_dt, int kv_dt, int head_dim, int group);
 hipError_t launch_decode_mfma(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                               hipStream_t stream);
 
-// matrix-core kernel for large groups, G > 16 (decode_mqa.hip)
-bool decode_mqa_supported(int q_dt, int kv_dt, int head_dim, int group);
-hipError_t launch_decode_mqa(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
-                             hipStream_t stream);
+
 
 }  // namespace pa

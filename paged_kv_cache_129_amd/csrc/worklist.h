@@ -1,11 +1,11 @@
 // How the decode kernels share out their work.
 //
 // A "segment" is the context of one (sequence, unit), where a unit is what
-// one work item computes for: one query head (per-head kernel) or one KV head
-// with all the query heads of its group (grouped kernels).  Items are taken by
-// "workers": single wavefronts in the per-head and grouped kernels (each
-// streams its own items, so one wavefront's wait for memory never idles its
-// neighbours), whole workgroups in the large-group kernel.  Wavefront w of
+// one work item computes for: one query head (per-head kernel), or one KV head
+// with all (or, for very large groups, an equal share) of the query heads that
+// read it (matrix-core kernel).  Items are taken by
+// "workers": single wavefronts (each streams its own items, so one
+// wavefront's wait for memory never idles its neighbours).  Wavefront w of
 // workgroup b is worker b * NW + w (measured: spreading consecutive workers
 // over workgroups instead is no faster for ragged batches and slower for
 // uniform ones).  Launches are persistent: the grid is what the GPU holds at
@@ -160,7 +160,7 @@ __device__ __forceinline__ int locate(const T* pref, int n, T x) {
 template <int NT>
 struct Schedule {
     const int32_t* ctx;     // [n] clamped context lengths
-    int s0, n, units, G;
+    int s0, n, units, G;    // G: partial-record slots per unit
     // partitions
     const int32_t* pref;    // [n+1] exclusive prefix of non-last partitions
     const int32_t* order;   // [n] sequences by last-partition class, longest first
@@ -178,7 +178,7 @@ struct Schedule {
         units = units_;
         worker = uni(worker_);
         workers = workers_;
-        G = a.num_heads / units_;
+        G = a.unit_heads;
         int32_t* ctxw = lds;
         const int per = (n + NT - 1) / NT;
         const int beg = min(n, (int)threadIdx.x * per);
@@ -335,7 +335,9 @@ struct Schedule {
         it.t0 = part * a.part_tokens;
         it.t1 = min(it.ctx, it.t0 + a.part_tokens);
         it.whole = parts_of(it.ctx, a.part_tokens) == 1;
-        it.rec0 = ((int64_t)it.s * a.num_heads + (int64_t)unit * G) * a.num_parts + part;
+        const int64_t head0 = (int64_t)(unit / a.units_per_kv) * (a.num_heads / a.num_kv_heads) +
+                              (int64_t)(unit % a.units_per_kv) * a.unit_heads;
+        it.rec0 = ((int64_t)it.s * a.num_heads + head0) * a.num_parts + part;
         it.rec_stride = a.num_parts;
         return true;
     }

@@ -103,18 +103,19 @@ def test_workspace_size():
     assert ws(4, 8, 8, 128, 512, 512) == 0
     # split-context: (max, sum, output) per (sequence, head, partition)
     assert ws(4, 8, 8, 128, 1025, 512) == r256(4 * 8 * 3 * 130 * 4)
-    # balanced: two records of a unit's heads per worker, at most 32 workers
-    # per CU (16 when a KV head serves more than 16 query heads; MI355X: 256
-    # CUs, also the fallback without a device), then one 6-word range
-    # descriptor per worker (32 per CU); all per started window of 1024 sequences
+    # balanced: two records of a work unit's heads per worker, at most 32 workers
+    # (wavefronts) per CU (MI355X: 256 CUs, also the fallback without a device),
+    # then one 6-word range descriptor per worker; all per started window of 1024
+    # sequences.  A unit holds all G query heads of a KV head up to G = 16, else
+    # whole 16-head tiles (up to 5 per unit at head_dim 64, 2 at head_dim 128).
     cus = 256
-    for S, H, Hkv, D in ((4, 8, 2, 128), (4, 32, 32, 64), (1500, 71, 1, 64)):
+    for S, H, Hkv, D, unit in ((4, 8, 2, 128, 4), (4, 32, 32, 64, 1), (1500, 71, 1, 64, 80),
+                               (4, 128, 1, 64, 64), (4, 100, 1, 128, 32), (4, 20, 1, 128, 32)):
         windows = (S + 1023) // 1024
-        group = H // Hkv if H // Hkv >= 2 else 1
-        workers = cus * (16 if group > 16 else 32)
-        expect = r256(windows * workers * 2 * group * (D + 2) * 4) + \
-            r256(windows * cus * 32 * 6 * 8)
-        assert ws(S, H, Hkv, D, 100, -1) == expect
+        workers = cus * 32
+        expect = r256(windows * workers * 2 * unit * (D + 2) * 4) + \
+            r256(windows * workers * 6 * 8)
+        assert ws(S, H, Hkv, D, 100, -1) == expect, (S, H, Hkv, D)
     assert ws(0, 8, 8, 128, 100, 0) == 0
     assert ws(4, 8, 8, 128, 100, -2) == 0
 
