@@ -287,9 +287,8 @@ class Tiny(HostLayers):
 
 
 # launch configuration per workload: the fastest measured on MI355X (uniform
-# long contexts: one pass per (sequence, head); ragged batches: balanced split;
-# the large-group kernel: 512-token partitions)
-DEFAULT_PARTITION = {"llama7b": 0, "opt13b": -1, "falcon7b": 512, "llama70b": -1, "tiny": 0}
+# long contexts: one pass per (sequence, head); ragged batches: balanced split)
+DEFAULT_PARTITION = {"llama7b": 0, "opt13b": -1, "falcon7b": -1, "llama70b": -1, "tiny": 0}
 
 WORKLOADS = {"llama7b": Llama7B, "opt13b": Opt13B, "falcon7b": Falcon7B, "llama70b": Llama70B,
              "tiny": Tiny}

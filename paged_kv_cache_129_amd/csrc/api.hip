@@ -73,10 +73,10 @@ size_t balanced_desc_bytes(int64_t num_seqs) {
 // record slots per work unit: the matrix-core kernel's unit heads when it may
 // run (2 <= G <= kMaxGroup), else one head (per-head kernel); an upper bound
 // whichever kernel the data types select
-int64_t unit_group(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim) {
+int64_t unit_group(int32_t num_heads, int32_t num_kv_heads) {
     if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return 1;
     const int g = num_heads / num_kv_heads;
-    return g >= 2 && g <= pa::kMaxGroup ? pa::mfma_unit_heads(g, head_dim) : 1;
+    return g >= 2 && g <= pa::kMaxGroup ? pa::mfma_unit_heads(g) : 1;
 }
 
 }  // namespace
@@ -152,7 +152,7 @@ size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, in
         max_context_len < 0 || (partition_size < 0 && partition_size != PA_PARTITION_BALANCED))
         return 0;
     if (partition_size == PA_PARTITION_BALANCED)
-        return balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads, head_dim), head_dim) +
+        return balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads), head_dim) +
                balanced_desc_bytes(num_seqs);
     return partial_bytes(num_seqs, num_heads, head_dim,
                          num_partitions(max_context_len, partition_size));
@@ -194,7 +194,7 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
     const int64_t parts = balanced ? 1 : num_partitions(ctx_cap, partition_size);
     if ((int64_t)num_seqs * num_heads * parts >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
     const size_t rec_bytes =
-        balanced ? balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads, head_dim), head_dim)
+        balanced ? balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads), head_dim)
                  : partial_bytes(num_seqs, num_heads, head_dim, parts);
     const size_t need =
         rec_bytes + (balanced ? balanced_desc_bytes(num_seqs) : 0);

@@ -95,7 +95,7 @@ __device__ __forceinline__ int dmap(int c, int j) {
     return 32 * c + 8 * j;
 }
 
-template <int KVDT, int QDT, int D, int NW, int TILES>
+template <int KVDT, int QDT, int D, int NW, int TILES, int PD>
 __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = (KVDT == PA_FP8_E4M3) ? PA_F16 : KVDT;   // MFMA operand type
     constexpr int EB = elem_bytes(KVDT);
@@ -340,16 +340,22 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
                     __builtin_amdgcn_wave_barrier();
                 };
 
-                constexpr int kStep = kChunk;
-                ChunkRegs ra, rb;
-                int c0 = ts;
-                load_chunk(ra, c0);
-                for (; c0 < te; c0 += 2 * kStep) {
-                    load_chunk(rb, c0 + kStep);
-                    compute_chunk(ra, c0);
-                    if (c0 + kStep >= te) break;
-                    load_chunk(ra, c0 + 2 * kStep);
-                    compute_chunk(rb, c0 + kStep);
+                // a ring of PD register sets: chunk i lives in set i mod PD, and the
+                // loads of chunk i + PD - 1 are issued just before chunk i is computed
+                ChunkRegs ring[PD];
+#pragma unroll
+                for (int k = 0; k < PD - 1; ++k) load_chunk(ring[k], ts + k * kChunk);
+                for (int c0 = ts; c0 < te; c0 += PD * kChunk) {
+                    bool done = false;
+#pragma unroll
+                    for (int k = 0; k < PD; ++k) {
+                        if (!done) {
+                            load_chunk(ring[(k + PD - 1) % PD], c0 + (k + PD - 1) * kChunk);
+                            compute_chunk(ring[k], c0 + k * kChunk);
+                            done = c0 + (k + 1) * kChunk >= te;
+                        }
+                    }
+                    if (done) break;
                 }
             }
 
@@ -393,7 +399,8 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
 template <int KVDT, int QDT, int D, int TILES>
 hipError_t launch_tiles(DecodeArgs& a, hipStream_t stream) {
     constexpr int NW = 4;
-    auto kernel = decode_mfma_kernel<KVDT, QDT, D, NW, TILES>;
+    constexpr int PD = 2;       // chunks in flight per wavefront (deeper rings measured no faster)
+    auto kernel = decode_mfma_kernel<KVDT, QDT, D, NW, TILES, PD>;
     const int G = a.num_heads / a.num_kv_heads;
     a.unit_heads = G <= 16 ? G : 16 * TILES;
     a.units_per_kv = (G + a.unit_heads - 1) / a.unit_heads;
@@ -405,16 +412,9 @@ hipError_t launch_tiles(DecodeArgs& a, hipStream_t stream) {
 
 template <int KVDT, int QDT, int D>
 hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
-    switch (mfma_tiles(a.num_heads / a.num_kv_heads, D)) {
+    switch (mfma_tiles(a.num_heads / a.num_kv_heads)) {
         case 1: return launch_tiles<KVDT, QDT, D, 1>(a, stream);
         case 2: return launch_tiles<KVDT, QDT, D, 2>(a, stream);
-    }
-    if constexpr (D == 64) {
-        switch (mfma_tiles(a.num_heads / a.num_kv_heads, D)) {
-            case 3: return launch_tiles<KVDT, QDT, D, 3>(a, stream);
-            case 4: return launch_tiles<KVDT, QDT, D, 4>(a, stream);
-            case 5: return launch_tiles<KVDT, QDT, D, 5>(a, stream);
-        }
     }
     return hipErrorInvalidValue;
 }

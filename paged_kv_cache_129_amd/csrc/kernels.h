@@ -46,19 +46,21 @@ constexpr int kDescWords = 6;
 // 32 wavefronts per CU at most, each a worker
 constexpr int kMaxWorkersPerCu = 32;
 
-// Matrix-core kernel: a wavefront computes up to 5 (head_dim 64) or 2 (head_dim
-// 128) 16-head tiles of one KV head's query heads from one read of K and V;
-// larger groups are split into units of equal tile counts.
+// Matrix-core kernel: a wavefront computes one or two 16-head tiles of one KV
+// head's query heads from one read of K and V; larger groups are split into
+// units of equal tile counts (whose reads of the same K and V mostly meet in
+// L2).  Measured on Falcon-7B's 71 heads: two tiles per wavefront beat one
+// (five reads) and three to five (one or two wavefronts per SIMD leave the
+// dependent matrix-core and softmax steps exposed).
 constexpr int kMaxGroup = 128;
-__host__ __device__ constexpr int mfma_tiles(int group, int head_dim) {
+__host__ __device__ constexpr int mfma_tiles(int group) {
     const int tiles = (group + 15) / 16;
-    const int tmax = head_dim == 64 ? 5 : 2;
-    const int units = (tiles + tmax - 1) / tmax;
+    const int units = (tiles + 1) / 2;
     return (tiles + units - 1) / units;
 }
 // query heads per work unit (record slots per unit) of the matrix-core kernel
-__host__ __device__ constexpr int mfma_unit_heads(int group, int head_dim) {
-    return group <= 16 ? group : 16 * mfma_tiles(group, head_dim);
+__host__ __device__ constexpr int mfma_unit_heads(int group) {
+    return group <= 16 ? group : 16 * mfma_tiles(group);
 }
 
 struct DecodeArgs {

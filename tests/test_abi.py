@@ -107,10 +107,11 @@ def test_workspace_size():
     # (wavefronts) per CU (MI355X: 256 CUs, also the fallback without a device),
     # then one 6-word range descriptor per worker; all per started window of 1024
     # sequences.  A unit holds all G query heads of a KV head up to G = 16, else
-    # whole 16-head tiles (up to 5 per unit at head_dim 64, 2 at head_dim 128).
+    # one or two whole 16-head tiles (equal counts per unit).
     cus = 256
-    for S, H, Hkv, D, unit in ((4, 8, 2, 128, 4), (4, 32, 32, 64, 1), (1500, 71, 1, 64, 80),
-                               (4, 128, 1, 64, 64), (4, 100, 1, 128, 32), (4, 20, 1, 128, 32)):
+    for S, H, Hkv, D, unit in ((4, 8, 2, 128, 4), (4, 32, 32, 64, 1), (1500, 71, 1, 64, 32),
+                               (4, 128, 1, 64, 32), (4, 100, 1, 128, 32), (4, 20, 1, 128, 32),
+                               (4, 48, 1, 64, 32), (4, 17, 1, 64, 32)):
         windows = (S + 1023) // 1024
         workers = cus * 32
         expect = r256(windows * workers * 2 * unit * (D + 2) * 4) + \
