@@ -95,8 +95,11 @@ __device__ __forceinline__ int dmap(int c, int j) {
     return 32 * c + 8 * j;
 }
 
+// One 16-head tile fits two wavefronts per SIMD (at most 256 registers each,
+// vector and accumulation together), which the bound below holds the
+// compiler to; two tiles need one wavefront's whole share.
 template <int KVDT, int QDT, int D, int NW, int TILES, int PD>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = (KVDT == PA_FP8_E4M3) ? PA_F16 : KVDT;   // MFMA operand type
     constexpr int EB = elem_bytes(KVDT);
     constexpr int NC = D / 32;               // score MFMAs per chunk and tile
