@@ -171,6 +171,11 @@ EDGE = [
     ("fp8_e4m3", "f16", 128, 16, 4, 2, [1, 16, 17, 333]),
     ("fp8_e4m3", "bf16", 64, 8, 8, 8, [2, 9, 1000]),
     ("fp8_e4m3", "f32", 64, 32, 3, 1, [5, 40, 97]),
+    # items longer than a wavefront's staged block-table slice (256 entries)
+    ("f16", "f16", 128, 1, 4, 4, [1, 700, 2100]),
+    ("f32", "f32", 64, 4, 2, 2, [4100, 3]),
+    ("bf16", "bf16", 128, 2, 8, 2, [600, 1500]),
+    ("fp8_e4m3", "f16", 64, 1, 71, 1, [300, 1100]),
 ]
 
 
