@@ -1,32 +1,32 @@
-// paged_attention_decode, matrix-core path for grouped heads (2 <= G <= 16
+// paged_attention_decode, matrix-core path for grouped heads (2 <= G <= 128
 // query heads per KV head).
 //
 // When several query heads share one KV head (KV 缓存与分页注意力 §11;
 // KV Cache从原理到实战 §5.3), one pass over a KV tile serves all G heads, and
 // scores = K·Q^T and out = P·V become small dense contractions on the matrix
-// cores: the G heads (padded to 16) are one MFMA dimension, 16 tokens another.
+// cores: the heads (padded to 16, or cut into units of 16 or 32 for large
+// groups) are one MFMA dimension, 16 tokens another.
 //
-// A work item = (sequence, KV head, partition), taken from the compact work
-// list of worklist.h; the workgroup's NW wavefronts take interleaved 16-token
-// chunks of it.  Per chunk a wavefront
+// Work items come from worklist.h; each wavefront is a worker that streams
+// its items in 16-token chunks.  Per chunk it
 //   * loads the 16 K rows straight into the A-operand layout of
 //     v_mfma_f32_16x16x32 (lane = token row, eight consecutive head_dim numbers
 //     per lane, 16-byte loads) and computes S^T[token][head];
-//   * runs the online softmax per head column (running max in log2 units,
-//     shared by a column's four lanes through two shuffles; the running sum
-//     stays per lane and is added up at the end);
+//   * runs the online softmax per head column (running maximum in log2 units,
+//     combined over a column's four lanes by two lane-row swaps; the running
+//     sum stays per lane and is added up at the end); the reference maximum
+//     moves only when a score passes it by more than kMaxSlack, so the
+//     accumulators are rescaled only on the rare chunks where it moves;
 //   * stages its V rows in its own LDS slice (rows of absent tokens zeroed)
-//     and reads them back transposed as the A operand of the K=16 MFMA
-//     O^T[d][head] += V^T·P^T, whose B operand is exactly the register layout
-//     the score MFMA produced (for bf16, P is split into a bf16 high and low
-//     part so the weights keep ~16 significant bits).
-// Everything around the loads is branch-free (masks are selects), which keeps
-// the compiler's wait counts exact; 16-token chunks keep the register budget
-// low enough for four wavefronts per SIMD, whose loads overlap each other's
-// compute.  The wavefronts' states are merged through LDS (log-sum-exp merge);
-// with several partitions the result goes to the workspace and the reduction
-// kernel of decode.hip finishes it.  An fp8 cache is widened to fp16 in
-// registers (value * 2^-8; the factor is folded into the scales).
+//     and reads them back with transposing LDS reads as the A operand of the
+//     K=16 MFMA O^T[d][head] += V^T·P^T, whose B operand is exactly the
+//     register layout the score MFMA produced (for bf16, P is split into a
+//     bf16 high and low part so the weights keep ~16 significant bits).
+// With blocks of 16 tokens or more a chunk lies in one block: its pool offset
+// is wavefront-uniform (one table lookup per chunk) and each lane adds a fixed
+// offset; smaller blocks take a per-token lookup.  The next chunk's loads are
+// issued before the current one is computed.  An fp8 cache is widened to fp16
+// in registers (value * 2^-8; the factor is folded into the scales).
 #include "kernels.h"
 #include "pa_device.h"
 #include "worklist.h"
@@ -43,6 +43,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kTableCap = 1024;     // block-table entries staged in LDS per segment
 constexpr int kChunk = 16;          // tokens per wavefront step
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kMaxSlack = 8.0f;   // log2 units a score may exceed the reference maximum by
 
 struct Op8 {                        // eight 16-bit MFMA operand values
     uint32_t w[4];
@@ -80,10 +81,45 @@ __device__ __forceinline__ uint32_t pack_f16(float a, float b) {
     return __builtin_bit_cast(uint32_t, h);
 }
 
+// two floats -> two bf16, round to nearest even (one v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
 template <int MT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     if constexpr (MT == PA_F16) return pack_f16(a, b);
-    return f32_to_bf16_bits(a) | (f32_to_bf16_bits(b) << 16);
+    return pack_bf16(a, b);
+}
+
+// Lane-group reductions of a value held per (lane group j, column c16): the
+// four lanes c16, c16+16, c16+32, c16+48 combine through two swaps between
+// lane rows (v_permlane16_swap, v_permlane32_swap), with no LDS round trip.
+__device__ __forceinline__ float max_over_groups(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_over_groups(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes,
+// lane 4k + q gives the address of four consecutive 16-bit values, and lane i
+// receives value i % 4 from lane 4k + i / 4, for k = 0..3.  With lane 4k + q
+// of group g pointing at row 4g + k, columns 4q..4q+3 of a row-major tile,
+// lane i of group g receives rows 4g..4g+3 of column i: an MFMA operand whose
+// four K values run down a column.
+__device__ __forceinline__ Op4 read_tr16(const uint16_t* p) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef s16x4 __attribute__((address_space(3))) * lds_ptr;
+    return __builtin_bit_cast(Op4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_ptr)p));
 }
 
 // head_dim offset of score-operand chunk c for lane group j (the same mapping
@@ -98,7 +134,7 @@ __device__ __forceinline__ int dmap(int c, int j) {
 // One 16-head tile fits two wavefronts per SIMD (at most 256 registers each,
 // vector and accumulation together), which the bound below holds the
 // compiler to; two tiles need one wavefront's whole share.
-template <int KVDT, int QDT, int D, int NW, int TILES, int PD>
+template <int KVDT, int QDT, int D, int NW, int TILES, int PD, bool BIGB>
 __global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = (KVDT == PA_FP8_E4M3) ? PA_F16 : KVDT;   // MFMA operand type
     constexpr int EB = elem_bytes(KVDT);
@@ -204,51 +240,78 @@ __global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kerne
                 const int te = min(t1, se << a.log2_bs);
 
                 // pool row (token row index) of token t, or -1 when absent; branch-free,
-                // so that loads issued around it keep precise wait counts
+                // so that loads issued around it keep precise wait counts (blocks of
+                // fewer than 16 tokens, where a chunk spans several blocks)
                 auto row_of = [&](int t) -> int64_t {
                     const bool in = t < te;
                     const int blk = tbl[in ? (t >> a.log2_bs) - sb : 0];
                     const int64_t r = (((int64_t)blk * a.num_kv_heads + kvh) << a.log2_bs) + (t & (bs - 1));
                     return (in && blk >= 0) ? r : (int64_t)-1;
                 };
+                // blocks of 16 tokens or more: chunks are 16-aligned windows, so a chunk
+                // lies in one block; its byte offset in the pool is wavefront-uniform
+                // and every lane adds a fixed offset of its own
+                const int c_begin = BIGB ? (ts & ~(kChunk - 1)) : ts;
+                auto chunk_off = [&](int c0, bool& valid) -> int64_t {
+                    const bool in = c0 < te;
+                    const int blk = __builtin_amdgcn_readfirstlane(tbl[in ? (c0 >> a.log2_bs) - sb : 0]);
+                    valid = in && blk >= 0;
+                    return (((int64_t)(valid ? blk : 0) * a.num_kv_heads + kvh) << a.log2_bs) * row_bytes +
+                           (int64_t)(c0 & (bs - 1)) * row_bytes;
+                };
+                const uint32_t k_lane = (uint32_t)(c16 * row_bytes) +
+                                        (KVDT == PA_FP8_E4M3 ? (D / 4) * j : 16 * j);
+                const uint32_t v_lane = (uint32_t)((lane / PPR) * row_bytes + (lane % PPR) * 16);
 
                 // One chunk's K operands and raw V pieces.  Two sets alternate: the next
-                // chunk's loads are always issued (past the end they read row 0 and are
-                // masked) before the current chunk is computed, so they overlap it and
-                // no branch sits between a load and its wait.
+                // chunk's loads are always issued (past the end they read the pool's
+                // first block and are masked) before the current chunk is computed, so
+                // they overlap it and no branch sits between a load and its wait.
                 struct ChunkRegs {
                     Op8 k[NC];
                     Raw16 v[NPV];
                     bool vlive[NPV];
+                    bool valid;
                 };
                 auto load_chunk = [&](ChunkRegs& R, int c0) {
-                    {
+                    const char* krow;
+                    const char* vrow[NPV];
+                    if constexpr (BIGB) {
+                        const int64_t off = chunk_off(c0, R.valid);
+                        krow = kbase + off + k_lane;
+#pragma unroll
+                        for (int u = 0; u < NPV; ++u)
+                            vrow[u] = vbase + off + v_lane + (uint32_t)(u * (64 / PPR) * row_bytes);
+                    } else {
                         const int64_t r = row_of(c0 + c16);
-                        const char* krow = kbase + (r < 0 ? 0 : r) * row_bytes;
-                        if constexpr (KVDT == PA_FP8_E4M3) {
+                        krow = kbase + (r < 0 ? 0 : r) * row_bytes +
+                               (KVDT == PA_FP8_E4M3 ? (D / 4) * j : 16 * j);
 #pragma unroll
-                            for (int hh = 0; hh < D / 64; ++hh) {
-                                const Raw16 raw = load16_stream(krow + (D / 4) * j + 16 * hh);
-                                // keep the raw codes; widened when used
+                        for (int u = 0; u < NPV; ++u) {
+                            const int p = u * 64 + lane;
+                            const int64_t rv = row_of(c0 + p / PPR);
+                            R.vlive[u] = rv >= 0;
+                            vrow[u] = vbase + (rv < 0 ? 0 : rv) * row_bytes + (p % PPR) * 16;
+                        }
+                    }
+                    if constexpr (KVDT == PA_FP8_E4M3) {
 #pragma unroll
-                                for (int q = 0; q < 4; ++q) R.k[2 * hh + (q >> 1)].w[(q & 1) * 2] = raw.w[q];
-                            }
-                        } else {
+                        for (int hh = 0; hh < D / 64; ++hh) {
+                            const Raw16 raw = load16_stream(krow + 16 * hh);
+                            // keep the raw codes; widened when used
 #pragma unroll
-                            for (int c = 0; c < NC; ++c) {
-                                const Raw16 raw = load16_stream(krow + dmap<KVDT, D>(c, j) * 2);
+                            for (int q = 0; q < 4; ++q) R.k[2 * hh + (q >> 1)].w[(q & 1) * 2] = raw.w[q];
+                        }
+                    } else {
 #pragma unroll
-                                for (int q = 0; q < 4; ++q) R.k[c].w[q] = raw.w[q];
-                            }
+                        for (int c = 0; c < NC; ++c) {
+                            const Raw16 raw = load16_stream(krow + 64 * c);
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) R.k[c].w[q] = raw.w[q];
                         }
                     }
 #pragma unroll
-                    for (int u = 0; u < NPV; ++u) {
-                        const int p = u * 64 + lane;
-                        const int64_t r = row_of(c0 + p / PPR);
-                        R.vlive[u] = r >= 0;
-                        R.v[u] = load16_stream(vbase + (r < 0 ? 0 : r) * row_bytes + (p % PPR) * 16);
-                    }
+                    for (int u = 0; u < NPV; ++u) R.v[u] = load16_stream(vrow[u]);
                 };
                 auto compute_chunk = [&](ChunkRegs& R, int c0) {
                     Op8 kop[NC];
@@ -261,9 +324,20 @@ __global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kerne
                             kop[c] = R.k[c];
                         }
                     }
+                    // token liveness: a whole chunk of present tokens needs no masks
+                    bool full = false;
                     bool live[4];
+                    if constexpr (BIGB) {
+                        full = R.valid && c0 >= ts && c0 + kChunk <= te;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) live[i] = row_of(c0 + 4 * j + i) >= 0;
+                        for (int i = 0; i < 4; ++i) {
+                            const int t = c0 + 4 * j + i;
+                            live[i] = R.valid && t >= ts && t < te;
+                        }
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) live[i] = row_of(c0 + 4 * j + i) >= 0;
+                    }
 
                     // ---- per tile: scores S^T[token][head], online softmax per head column
                     Op4 pop[TILES], plo[TILES];
@@ -279,10 +353,14 @@ __global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kerne
                             sv[i] = live[i] ? sc[i] * a.qk_scale : kNegInf;
                             mx = fmaxf(mx, sv[i]);
                         }
-                        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-                        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-                        const float mn = fmaxf(m[tt], mx);
-                        const float alpha = (m[tt] == kNegInf) ? 0.0f : fast_exp2(m[tt] - mn);
+                        mx = max_over_groups(mx);
+                        // the reference maximum moves only when a score passes it by more
+                        // than kMaxSlack (weights then stay below 2^kMaxSlack), so the
+                        // accumulators are rarely rescaled
+                        const float mn = (mx > m[tt] + kMaxSlack) ? mx : m[tt];
+                        const bool moved = mn != m[tt];
+                        // (moving from -inf gives exp2(-inf) = 0)
+                        const float alpha = moved ? fast_exp2(m[tt] - mn) : 1.0f;
                         float pr[4];
                         float psum = 0.0f;
 #pragma unroll
@@ -292,8 +370,10 @@ __global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kerne
                         }
                         l[tt] = l[tt] * alpha + psum;
                         m[tt] = mn;
+                        if (__builtin_amdgcn_ballot_w64(moved)) {
 #pragma unroll
-                        for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] *= alpha;
+                            for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] *= alpha;
+                        }
                         pop[tt].w[0] = pack2<MT>(pr[0], pr[1]);
                         pop[tt].w[1] = pack2<MT>(pr[2], pr[3]);
                         if constexpr (MT == PA_BF16) {
@@ -312,28 +392,36 @@ __global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kerne
                     for (int u = 0; u < NPV; ++u) {
                         const int p = u * 64 + lane;
                         uint16_t* dst = vs + (p / PPR) * LDV + (p % PPR) * VEL;
+                        if constexpr (BIGB) {
+                            const int t = c0 + p / PPR;
+                            R.vlive[u] = full || (R.valid && t >= ts && t < te);
+                        }
                         if constexpr (KVDT == PA_FP8_E4M3) {
                             uint32_t wv[8];
 #pragma unroll
                             for (int q = 0; q < 4; ++q) e4m3x4_to_f16x4(R.v[u].w[q], wv[2 * q], wv[2 * q + 1]);
+                            if (!full) {
 #pragma unroll
-                            for (int q = 0; q < 8; ++q) wv[q] = R.vlive[u] ? wv[q] : 0u;
+                                for (int q = 0; q < 8; ++q) wv[q] = R.vlive[u] ? wv[q] : 0u;
+                            }
                             *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
                             *reinterpret_cast<uint4*>(dst + 8) = make_uint4(wv[4], wv[5], wv[6], wv[7]);
                         } else {
                             uint32_t wv[4];
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) wv[q] = R.vlive[u] ? R.v[u].w[q] : 0u;
+                            for (int q = 0; q < 4; ++q) wv[q] = R.v[u].w[q];
+                            if (!full) {
+#pragma unroll
+                                for (int q = 0; q < 4; ++q) wv[q] = R.vlive[u] ? wv[q] : 0u;
+                            }
                             *reinterpret_cast<uint4*>(dst) = make_uint4(wv[0], wv[1], wv[2], wv[3]);
                         }
                     }
                     __builtin_amdgcn_wave_barrier();
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
-                        const uint16_t* col = vs + 4 * j * LDV + 16 * dt + c16;
-                        Op4 vop;
-                        vop.w[0] = (uint32_t)col[0] | ((uint32_t)col[LDV] << 16);
-                        vop.w[1] = (uint32_t)col[2 * LDV] | ((uint32_t)col[3 * LDV] << 16);
+                        // V^T[d][token]: column d = 16 dt + c16, tokens 4j..4j+3
+                        const Op4 vop = read_tr16(vs + (4 * j + (c16 >> 2)) * LDV + 16 * dt + 4 * (c16 & 3));
 #pragma unroll
                         for (int tt = 0; tt < TILES; ++tt) {
                             acc[tt][dt] = mma16<MT>(vop, pop[tt], acc[tt][dt]);
@@ -347,8 +435,8 @@ __global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kerne
                 // loads of chunk i + PD - 1 are issued just before chunk i is computed
                 ChunkRegs ring[PD];
 #pragma unroll
-                for (int k = 0; k < PD - 1; ++k) load_chunk(ring[k], ts + k * kChunk);
-                for (int c0 = ts; c0 < te; c0 += PD * kChunk) {
+                for (int k = 0; k < PD - 1; ++k) load_chunk(ring[k], c_begin + k * kChunk);
+                for (int c0 = c_begin; c0 < te; c0 += PD * kChunk) {
                     bool done = false;
 #pragma unroll
                     for (int k = 0; k < PD; ++k) {
@@ -366,8 +454,7 @@ __global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kerne
 #pragma unroll
             for (int tt = 0; tt < TILES; ++tt) {
                 float lt = l[tt];
-                lt += __shfl_xor(lt, 16, 64);
-                lt += __shfl_xor(lt, 32, 64);
+                lt = sum_over_groups(lt);
                 const int hu = 16 * tt + c16;
                 if (hu < nh) {
                     const int head = kvh * G + hg0 + hu;
@@ -403,7 +490,8 @@ template <int KVDT, int QDT, int D, int TILES>
 hipError_t launch_tiles(DecodeArgs& a, hipStream_t stream) {
     constexpr int NW = 4;
     constexpr int PD = 2;       // chunks in flight per wavefront (deeper rings measured no faster)
-    auto kernel = decode_mfma_kernel<KVDT, QDT, D, NW, TILES, PD>;
+    auto kernel = a.log2_bs >= 4 ? decode_mfma_kernel<KVDT, QDT, D, NW, TILES, PD, true>
+                                 : decode_mfma_kernel<KVDT, QDT, D, NW, TILES, PD, false>;
     const int G = a.num_heads / a.num_kv_heads;
     a.unit_heads = G <= 16 ? G : 16 * TILES;
     a.units_per_kv = (G + a.unit_heads - 1) / a.unit_heads;
