@@ -131,11 +131,13 @@ __device__ __forceinline__ int dmap(int c, int j) {
     return 32 * c + 8 * j;
 }
 
-// One 16-head tile fits two wavefronts per SIMD (at most 256 registers each,
-// vector and accumulation together), which the bound below holds the
-// compiler to; two tiles need one wavefront's whole share.
+// One wavefront per SIMD may take all its registers: measured on Llama-2-70B
+// (one 16-head tile), one wavefront per SIMD with three chunks in flight beats
+// two wavefronts per SIMD with two (108 vs 114 us per layer): of two
+// wavefronts sharing a SIMD the older one gets most of the memory pipeline,
+// and the younger one finishes its equal share well after it.
 template <int KVDT, int QDT, int D, int NW, int TILES, int PD, bool BIGB>
-__global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int MT = (KVDT == PA_FP8_E4M3) ? PA_F16 : KVDT;   // MFMA operand type
     constexpr int EB = elem_bytes(KVDT);
     constexpr int NC = D / 32;               // score MFMAs per chunk and tile
@@ -489,7 +491,7 @@ __global__ __launch_bounds__(NW * 64, TILES == 1 ? 2 : 1) void decode_mfma_kerne
 template <int KVDT, int QDT, int D, int TILES>
 hipError_t launch_tiles(DecodeArgs& a, hipStream_t stream) {
     constexpr int NW = 4;
-    constexpr int PD = 2;       // chunks in flight per wavefront (deeper rings measured no faster)
+    constexpr int PD = TILES == 1 ? 3 : 2;   // chunks in flight per wavefront (measured best)
     auto kernel = a.log2_bs >= 4 ? decode_mfma_kernel<KVDT, QDT, D, NW, TILES, PD, true>
                                  : decode_mfma_kernel<KVDT, QDT, D, NW, TILES, PD, false>;
     const int G = a.num_heads / a.num_kv_heads;
