@@ -82,29 +82,29 @@ __device__ __forceinline__ uint64_t shfl_up64(uint64_t v, int d) {
     return ((uint64_t)hi << 32) | lo;
 }
 
-// Inclusive prefix sums over the workgroup of three 64-bit values (wavefront
+// Inclusive prefix sums over the workgroup of Q 64-bit values (wavefront
 // shuffles, then one exchange of wavefront totals through LDS); `tot` gets the
 // workgroup totals.
-template <int NT>
-__device__ __forceinline__ void block_scan3(uint64_t v[3], uint64_t tot[3]) {
+template <int NT, int Q>
+__device__ __forceinline__ void block_scan(uint64_t v[Q], uint64_t tot[Q]) {
     constexpr int NW = NT / 64;
-    __shared__ uint64_t wsum[3][NW];
+    __shared__ uint64_t wsum[Q][NW];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
+        for (int q = 0; q < Q; ++q) {
             const uint64_t u = shfl_up64(v[q], d);
             if (lane >= d) v[q] += u;
         }
     }
     if (lane == 63) {
 #pragma unroll
-        for (int q = 0; q < 3; ++q) wsum[q][wave] = v[q];
+        for (int q = 0; q < Q; ++q) wsum[q][wave] = v[q];
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
+    for (int q = 0; q < Q; ++q) {
         uint64_t before = 0, all = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
@@ -141,13 +141,30 @@ struct Item {
     int rec_stride;
 };
 
-// largest i in [0, n) with pref[i] <= x (pref ascending, pref[0] == 0)
+// x / y for 0 <= x and 0 < y, in 32 bits when both fit (the common case)
+__device__ __forceinline__ int64_t udiv(int64_t x, int64_t y) {
+    if (x <= INT32_MAX && y <= INT32_MAX) return (int64_t)((uint32_t)x / (uint32_t)y);
+    return x / y;
+}
+
+// largest i in [0, n) with pref[i] <= x (pref ascending, pref[0] == 0); called
+// by all lanes of a wavefront with the same arguments
 template <typename T>
 __device__ __forceinline__ int locate(const T* pref, int n, T x) {
-    int lo = 0, hi = n;                 // invariant: pref[lo] <= x, and x < pref[hi] if hi < n
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (pref[mid] <= x) lo = mid; else hi = mid;
+    // the whole wavefront searches: each pass compares 64 evenly spaced entries
+    // at once and keeps the interval after the last one <= x (pref[0] <= x, so
+    // lane 0 always qualifies); invariant: pref[lo] <= x, and x < pref[lo + len]
+    // if lo + len < n
+    const int lane = threadIdx.x & 63;
+    int lo = 0, len = n;
+    while (len > 1) {
+        const int step = (len + 63) >> 6;
+        const int i = lane * step;
+        const bool le = i < len && pref[lo + i] <= x;
+        const uint64_t b = __builtin_amdgcn_ballot_w64(le);
+        const int k = 63 - __builtin_clzll(b);
+        lo += k * step;
+        len = min(step, len - k * step);
     }
     return lo;
 }
@@ -186,14 +203,14 @@ struct Schedule {
         __syncthreads();                    // the previous window's metadata is no longer read
         if (a.part_tokens < 0) {            // balanced
             int64_t* sp = reinterpret_cast<int64_t*>(lds + kWindow);
-            uint64_t own[3] = {0, 0, 0}, tot[3];
+            uint64_t own[1] = {0}, tot[1];
             for (int i = beg; i < end; ++i) {
                 const int c = clamp_ctx(a.ctx_lens[s0 + i], a.ctx_cap);
                 ctxw[i] = c;
                 own[0] += (uint64_t)split_len(c);
             }
-            uint64_t inc[3] = {own[0], 0, 0};
-            block_scan3<NT>(inc, tot);
+            uint64_t inc[1] = {own[0]};
+            block_scan<NT, 1>(inc, tot);
             int64_t run = (int64_t)(inc[0] - own[0]);
             for (int i = beg; i < end; ++i) {
                 sp[i] = run;
@@ -208,18 +225,19 @@ struct Schedule {
             gend = min(T, g + range);
             __syncthreads();
             // where this worker's range starts, for the reduction
+            // (located by the whole wavefront; the lead lane stores it)
+            int64_t w0 = 0, w1 = 0, w2 = 0, w4 = 0;
+            if (g < gend) {
+                int sl, unit;
+                int64_t t0, L;
+                piece_at(g, sl, unit, t0, L);
+                w0 = (int64_t)(s0 + sl) | ((int64_t)unit << 32);
+                w1 = t0;
+                w2 = L;
+                w4 = ctx[sl];
+            }
             if (lead) {
                 int64_t* d = a.desc + ((int64_t)(s0 / kWindow) * workers + worker) * kDescWords;
-                int64_t w0 = 0, w1 = 0, w2 = 0, w4 = 0;
-                if (g < gend) {
-                    int sl, unit;
-                    int64_t t0, L;
-                    piece_at(g, sl, unit, t0, L);
-                    w0 = (int64_t)(s0 + sl) | ((int64_t)unit << 32);
-                    w1 = t0;
-                    w2 = L;
-                    w4 = ctx[sl];
-                }
                 d[0] = w0;
                 d[1] = w1;
                 d[2] = w2;
@@ -241,7 +259,7 @@ struct Schedule {
             own[1 + (k >> 2)] += (uint64_t)1 << (16 * (k & 3));
         }
         uint64_t inc[3] = {own[0], own[1], own[2]}, tot[3];
-        block_scan3<NT>(inc, tot);
+        block_scan<NT, 3>(inc, tot);
         auto field = [](const uint64_t* v, int k) -> int {
             return (int)((v[1 + (k >> 2)] >> (16 * (k & 3))) & 0xFFFFu);
         };
@@ -282,10 +300,10 @@ struct Schedule {
     // and g's offset t0 in it
     __device__ __forceinline__ void piece_at(int64_t g_, int& sl, int& unit, int64_t& t0,
                                              int64_t& L) const {
-        sl = locate<int64_t>(spref, n, g_ / units);
+        sl = locate<int64_t>(spref, n, udiv(g_, units));
         const int64_t off = g_ - spref[sl] * units;
         L = spref[sl + 1] - spref[sl];
-        unit = (int)(off / L);
+        unit = (int)udiv(off, L);
         t0 = off - unit * L;
     }
 
