@@ -49,18 +49,16 @@ __device__ __forceinline__ void store16(void* p, const Raw16& r) {
     *reinterpret_cast<uint4*>(p) = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
 }
 
-// Four e4m3 codes (one dword) -> four fp16 bit patterns holding value * 2^-8.
-// e4m3 has 4 exponent bits with bias 7, fp16 has 5 with bias 15: moving the
-// code's exponent and mantissa into the fp16 fields unchanged gives the same
-// significand with an exponent lowered by 8, and e4m3 subnormals land on fp16
-// subnormals with the same factor, so the widening is exact.  The e4m3 NaN
-// code becomes a finite fp16 (480 * 2^-8); such slots are never live.
+// Four e4m3 codes (one dword) -> four fp16 bit patterns holding value * 2^-8,
+// by gfx950's scaled conversion (v_cvt_scalef32_pk_f16_fp8, scale 2^-8).
+// Every finite e4m3 value times 2^-8 is an fp16 number (e4m3 subnormals land
+// on fp16 subnormals), so the widening is exact; it gives the same bits as
+// moving the code's exponent and mantissa into the fp16 fields (checked on
+// the GPU for all 256 codes).  NaN codes give NaN; absent tokens are masked
+// by selects, never by multiplication.
 __device__ __forceinline__ void e4m3x4_to_f16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
-    // place byte k of w in byte 1 / byte 3 of a word: 0x(b1)00(b0)00
-    const uint32_t x0 = __builtin_amdgcn_perm(0u, w, 0x010C000Cu);
-    const uint32_t x1 = __builtin_amdgcn_perm(0u, w, 0x030C020Cu);
-    lo = (x0 & 0x80008000u) | ((x0 >> 1) & 0x3F803F80u);
-    hi = (x1 & 0x80008000u) | ((x1 >> 1) & 0x3F803F80u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f / kFp8WidenFactor, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f / kFp8WidenFactor, true));
 }
 
 __device__ __forceinline__ void f16x2_to_f32(uint32_t w, float& a, float& b) {
@@ -85,13 +83,15 @@ __device__ __forceinline__ void unpack16(const Raw16& r, float* f) {
             f[2 * i] = __uint_as_float(r.w[i] << 16);
             f[2 * i + 1] = __uint_as_float(r.w[i] & 0xFFFF0000u);
         }
-    } else {
+    } else {   // e4m3 straight to fp32 (v_cvt_scalef32_pk_f32_fp8, same values)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint32_t lo, hi;
-            e4m3x4_to_f16x4(r.w[i], lo, hi);
-            f16x2_to_f32(lo, f[4 * i], f[4 * i + 1]);
-            f16x2_to_f32(hi, f[4 * i + 2], f[4 * i + 3]);
+            const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.w[i], 1.0f / kFp8WidenFactor, false);
+            const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.w[i], 1.0f / kFp8WidenFactor, true);
+            f[4 * i] = lo[0];
+            f[4 * i + 1] = lo[1];
+            f[4 * i + 2] = hi[0];
+            f[4 * i + 3] = hi[1];
         }
     }
 }
