@@ -345,6 +345,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
                     Op4 pop[TILES], plo[TILES];
 #pragma unroll
                     for (int tt = 0; tt < TILES; ++tt) {
+                        if (tt > 0 && 16 * tt >= nh) break;      // a tile with no heads of the unit
                         f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int c = 0; c < NC; ++c) sc = mma32<MT>(kop[c], qop[tt][c], sc);
@@ -426,6 +427,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
                         const Op4 vop = read_tr16(vs + (4 * j + (c16 >> 2)) * LDV + 16 * dt + 4 * (c16 & 3));
 #pragma unroll
                         for (int tt = 0; tt < TILES; ++tt) {
+                            if (tt > 0 && 16 * tt >= nh) break;
                             acc[tt][dt] = mma16<MT>(vop, pop[tt], acc[tt][dt]);
                             if constexpr (MT == PA_BF16) acc[tt][dt] = mma16<MT>(vop, plo[tt], acc[tt][dt]);
                         }
