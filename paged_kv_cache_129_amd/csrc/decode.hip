@@ -1,25 +1,23 @@
-// paged_attention_decode, vector-ALU path: one workgroup per (sequence,
-// query head, partition).
+// paged_attention_decode, vector-ALU path: one query head per work item.
 //
 // The new token's query is dotted with every cached key, the scores become
 // softmax weights, and the weighted sum of the cached values is the head's
 // output (KV Cache从原理到实战 §2.1); the keys and values are fetched block
 // by block through the sequence's block table (KV 缓存与分页注意力 §07 块表).
 //
-// Work split.  A wavefront reads a chunk of CH tokens per step: each 16-byte
+// Work split.  Items come from worklist.h; each wavefront is a worker that
+// streams its items.  It reads a chunk of CH tokens per step: each 16-byte
 // load covers VEC numbers of one token row, LPR = head_dim / VEC lanes cover
 // a row and one load instruction covers RPI = 64 / LPR consecutive token rows
 // (16-byte vector loads, coalesced within a (block, head) tile).  Each lane
 // keeps a running max / sum / fp32 accumulator (online softmax) over the
 // tokens of its own lane-row; the row's partial dot products are summed with
-// DPP, lane-rows are merged at the end with shuffles and the workgroup's
-// waves through LDS (log-sum-exp merge).  Scores are kept in log2 units so
-// that v_exp_f32 computes the exponentials.
+// DPP and lane-rows are merged with shuffles at the end of the item.  Scores
+// are kept in log2 units so that v_exp_f32 computes the exponentials.
 //
-// Split context: with more than one partition per sequence each workgroup
-// writes its partition's (max, sum, normalised output) to the workspace and
-// the reduction kernel below merges them; a sequence with one partition is
-// written directly.
+// A cut item (split context) writes its (max, sum, normalised output) to the
+// workspace and a reduction kernel below merges the pieces; an item that holds
+// a whole context writes the output directly.
 #include "kernels.h"
 #include "pa_device.h"
 #include "worklist.h"
