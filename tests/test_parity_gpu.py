@@ -443,3 +443,29 @@ def test_many_windows_and_workspace_reuse(kv, q, H, Hkv):
             assert err <= TOL[kv]
             assert np.array_equal(o, outs[0]), "launches differ"
         del g
+
+
+# ------------------------------------------------------------------ moving maxima
+# Scores that rise along the context, fall, or jump at scattered positions:
+# the running maximum of the online softmax moves (or stays) in every way the
+# kernels distinguish — moved by more or less than their slack, at chunk
+# starts or inside chunks, in single-pass, balanced and partitioned launches.
+DRIFT = [
+    # kv, q, H, Hkv
+    ("bf16", "bf16", 8, 1),
+    ("f16", "f16", 8, 1),
+    ("fp8_e4m3", "f16", 8, 1),
+    ("f16", "f16", 2, 2),
+    ("fp8_e4m3", "f16", 71, 1),
+]
+
+
+@pytest.mark.parametrize("drift", ["rising", "falling", "spikes"])
+@pytest.mark.parametrize("kv,q,H,Hkv", DRIFT)
+def test_score_drift(kv, q, H, Hkv, drift):
+    ctx = [1, 15, 16, 17, 300, 700]
+    case = W.make_decode_case(f"drift_{drift}_{kv}_{H}", "tiny", num_seqs=len(ctx), num_heads=H,
+                              num_kv_heads=Hkv, head_dim=128 if H <= 8 else 64, block_size=16,
+                              context_lens=ctx, kv_dtype=kv, q_dtype=q, spare_blocks=3,
+                              salt=H, key_drift=drift)
+    run_and_check(case, partitions=(0, -1, 64))

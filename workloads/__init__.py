@@ -197,8 +197,13 @@ def make_decode_case(name: str, config: str, *, num_seqs: int, num_heads: int, n
                      kv_dtype: str, q_dtype: str, num_blocks: Optional[int] = None,
                      value_scale: float = 1.0, layer: int = 0, partition_size: int = 0,
                      spare_blocks: int = 0, append: bool = True, salt: int = 0,
-                     max_blocks: Optional[int] = None) -> DecodeCase:
-    """Build one case: shuffled placement, N(0,1)*value_scale values, poison elsewhere."""
+                     max_blocks: Optional[int] = None, key_drift: Optional[str] = None) -> DecodeCase:
+    """Build one case: shuffled placement, N(0,1)*value_scale values, poison elsewhere.
+
+    ``key_drift`` adds a position-dependent amount c(t) to the first head_dim
+    component of every key, and 3.0 to that component of every query, so the
+    scores follow c: "rising" (c = t / 2), "falling" (c = (n - 1 - t) / 2 for a
+    context of n), or "spikes" (c = 12..24 at every 29th position, else 0)."""
     ctx = np.asarray(context_lens, dtype=np.int32)
     S, H, Hkv, D, bs = num_seqs, num_heads, num_kv_heads, head_dim, block_size
     assert ctx.shape == (S,) and H % Hkv == 0
@@ -216,12 +221,28 @@ def make_decode_case(name: str, config: str, *, num_seqs: int, num_heads: int, n
     src_dtype = q_dtype
     k_new32 = rng_for(config, layer, "knew", salt).standard_normal((S, Hkv, D), dtype=np.float32) \
         * np.float32(value_scale)
+    q32 = rng_for(config, layer, "q", salt).standard_normal((S, H, D), dtype=np.float32) \
+        * np.float32(value_scale)
+    if key_drift is not None:
+        def drift(t: np.ndarray, n: int) -> np.ndarray:
+            if key_drift == "rising":
+                return 0.5 * t
+            if key_drift == "falling":
+                return 0.5 * (n - 1 - t)
+            if key_drift == "spikes":
+                return np.where(t % 29 == 7, 12.0 + 3.0 * ((t // 29) % 5), 0.0)
+            raise ValueError(key_drift)
+        for s in range(S):
+            n = int(pre[s])
+            k_vals[s][:, :, 0] += drift(np.arange(n), int(ctx[s]))[:, None].astype(np.float32)
+            if ctx[s] > 0:
+                k_new32[s, :, 0] += np.float32(drift(np.array([int(ctx[s]) - 1]), int(ctx[s]))[0])
+        q32[:, :, 0] += np.float32(3.0)
     v_new32 = rng_for(config, layer, "vnew", salt).standard_normal((S, Hkv, D), dtype=np.float32) \
         * np.float32(value_scale)
     k_new = to_storage(k_new32, src_dtype)
     v_new = to_storage(v_new32, src_dtype)
-    q = to_storage(rng_for(config, layer, "q", salt).standard_normal((S, H, D), dtype=np.float32)
-                   * np.float32(value_scale), q_dtype)
+    q = to_storage(q32, q_dtype)
 
     k_scale = v_scale = 1.0
     if kv_dtype == "fp8_e4m3":
