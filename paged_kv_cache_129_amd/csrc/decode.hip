@@ -455,6 +455,7 @@ int device_cus() {
 
 int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers, DecodeArgs& a) {
     a.units = units;
+    a.simds = device_cus() * 4;                         // four SIMDs per compute unit
     const int per_wg = wave_workers ? threads / 64 : 1;
     int64_t grid;
     if (a.part_tokens < 0) {

@@ -72,13 +72,14 @@ struct DecodeArgs {
     const int32_t* ctx_lens;
     float* ws;                  // partial records: m[nrec], l[nrec], o[nrec][head_dim]
     int64_t nrec;               // partial records in ws (set with the grid when balanced)
-    int64_t* desc;              // balanced: 4 words per (window, workgroup) for the reduction
+    int64_t* desc;              // balanced: kDescWords per (window, worker) for the reduction
     int32_t units;              // work units per sequence (set at launch): a unit is
                                 // unit_heads query heads of KV head unit / units_per_kv,
                                 // from head (unit % units_per_kv) * unit_heads of its group
     int32_t units_per_kv;
     int32_t unit_heads;
     int32_t workers;            // workers of the attention launch (set at launch)
+    int32_t simds;              // SIMDs of the device (set at launch)
     int32_t num_seqs;
     int32_t num_heads;
     int32_t num_kv_heads;

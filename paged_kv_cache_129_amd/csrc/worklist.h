@@ -220,7 +220,18 @@ struct Schedule {
             spref = sp;
             ctx = ctxw;
             const int64_t T = uni((int64_t)tot[0] * units);
-            range = uni(split_range(T, workers));
+            // with less than kMinRange tokens per worker, only some workers get a
+            // range: a whole number per SIMD where there are enough (workers are
+            // block-major and a workgroup's wavefronts sit on different SIMDs, so
+            // the first k * SIMDs workers put k on every SIMD), else one each
+            int64_t active = workers;
+            if (T < (int64_t)workers * kMinRange) {
+                const int64_t simds = a.simds > 0 ? a.simds : 1;
+                active = T / ((int64_t)kMinRange * simds) * simds;
+                if (active == 0) active = (T + kMinRange - 1) / kMinRange;
+                active = max((int64_t)1, min(active, (int64_t)workers));
+            }
+            range = uni(split_range(T, active));
             g = min(T, (int64_t)worker * range);
             gend = min(T, g + range);
             __syncthreads();
