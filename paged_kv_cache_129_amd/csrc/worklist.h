@@ -67,8 +67,14 @@ __device__ __forceinline__ int64_t split_run(int ctx) {
 __device__ __forceinline__ int64_t split_len(int ctx) { return split_run(ctx) + kSegCost; }
 
 // balanced: tokens per worker range for T padded tokens over `grid` workers
+// x / y for 0 <= x and 0 < y, in 32 bits when both fit (the common case)
+__device__ __forceinline__ int64_t udiv(int64_t x, int64_t y) {
+    if (x <= INT32_MAX && y <= INT32_MAX) return (int64_t)((uint32_t)x / (uint32_t)y);
+    return x / y;
+}
+
 __device__ __forceinline__ int64_t split_range(int64_t T, int64_t grid) {
-    int64_t r = (T + grid - 1) / grid;
+    int64_t r = udiv(T + grid - 1, grid);
     r = (r + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
     return r < kMinRange ? kMinRange : r;
 }
@@ -141,12 +147,6 @@ struct Item {
     int rec_stride;
 };
 
-// x / y for 0 <= x and 0 < y, in 32 bits when both fit (the common case)
-__device__ __forceinline__ int64_t udiv(int64_t x, int64_t y) {
-    if (x <= INT32_MAX && y <= INT32_MAX) return (int64_t)((uint32_t)x / (uint32_t)y);
-    return x / y;
-}
-
 // largest i in [0, n) with pref[i] <= x (pref ascending, pref[0] == 0); called
 // by all lanes of a wavefront with the same arguments
 template <typename T>
@@ -186,6 +186,8 @@ struct Schedule {
     // balanced
     const int64_t* spref;   // [n+1] exclusive prefix of padded segment lengths
     int64_t g, gend, range;
+    int64_t pg, pt0, pL;    // the piece located at range position pg (reused by next)
+    int psl, punit;
     int worker, workers;
 
     __device__ void build(const DecodeArgs& a, int s0_, int n_, int units_, int32_t* lds,
@@ -238,14 +240,14 @@ struct Schedule {
             // where this worker's range starts, for the reduction
             // (located by the whole wavefront; the lead lane stores it)
             int64_t w0 = 0, w1 = 0, w2 = 0, w4 = 0;
+            pg = -1;
             if (g < gend) {
-                int sl, unit;
-                int64_t t0, L;
-                piece_at(g, sl, unit, t0, L);
-                w0 = (int64_t)(s0 + sl) | ((int64_t)unit << 32);
-                w1 = t0;
-                w2 = L;
-                w4 = ctx[sl];
+                piece_at(g, psl, punit, pt0, pL);
+                pg = g;
+                w0 = (int64_t)(s0 + psl) | ((int64_t)punit << 32);
+                w1 = pt0;
+                w2 = pL;
+                w4 = ctx[psl];
             }
             if (lead) {
                 int64_t* d = a.desc + ((int64_t)(s0 / kWindow) * workers + worker) * kDescWords;
@@ -323,7 +325,14 @@ struct Schedule {
             while (g < gend) {
                 int sl, unit;
                 int64_t t0, L;
-                piece_at(g, sl, unit, t0, L);
+                if (g == pg) {              // the range's first piece, located by build
+                    sl = psl;
+                    unit = punit;
+                    t0 = pt0;
+                    L = pL;
+                } else {
+                    piece_at(g, sl, unit, t0, L);
+                }
                 const int64_t len = min(L - t0, gend - g);
                 const bool first = g == (int64_t)worker * range;
                 const int c = uni(ctx[sl]);
