@@ -353,6 +353,7 @@ hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
     constexpr int U = 4;
     auto kernel = decode_valu_kernel<KVDT, QDT, D, NW, U>;
     a.unit_heads = 1;                                   // a unit is one query head
+    a.seg_cost = 16;                                    // an item start, in tokens (measured)
     a.units_per_kv = a.num_heads / a.num_kv_heads;
     const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), NW * 64, a.num_heads, 1, a);
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NW * 64), 0, stream, a);

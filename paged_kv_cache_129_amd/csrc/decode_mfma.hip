@@ -498,6 +498,7 @@ hipError_t launch_tiles(DecodeArgs& a, hipStream_t stream) {
                                  : decode_mfma_kernel<KVDT, QDT, D, NW, TILES, PD, false>;
     const int G = a.num_heads / a.num_kv_heads;
     a.unit_heads = G <= 16 ? G : 16 * TILES;
+    a.seg_cost = 64;                                    // an item start, in tokens (measured)
     a.units_per_kv = (G + a.unit_heads - 1) / a.unit_heads;
     const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), NW * 64,
                                      a.num_kv_heads * a.units_per_kv, 1, a);

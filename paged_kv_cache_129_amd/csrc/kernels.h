@@ -80,6 +80,7 @@ struct DecodeArgs {
     int32_t unit_heads;
     int32_t workers;            // workers of the attention launch (set at launch)
     int32_t simds;              // SIMDs of the device (set at launch)
+    int32_t seg_cost;           // balanced: tokens' worth of cost per segment (set at launch)
     int32_t num_seqs;
     int32_t num_heads;
     int32_t num_kv_heads;

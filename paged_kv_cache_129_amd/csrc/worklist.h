@@ -22,8 +22,9 @@
 //   worker k mod W in even rounds and W-1-(k mod W) in odd ones (W workers).
 //
 // * Balanced (partition_size < 0): the window's segments, each padded to a
-//   multiple of kSplitAlign tokens plus kSegCost tokens that stand for the
-//   fixed cost of starting an item (they hold no tokens), are laid end to end
+//   multiple of kSplitAlign tokens plus seg_cost tokens that stand for the
+//   fixed cost of starting an item (they hold no tokens; the kernel sets it),
+//   are laid end to end
 //   and cut into one equal range per worker, so every worker gets the same
 //   cost whatever the length mix, and every CU and XCD the same load.  A
 //   worker that holds all of a segment's tokens writes its result straight to
@@ -42,7 +43,6 @@ namespace pa {
 
 constexpr int kClasses = 8;         // length classes of last partitions
 constexpr int kSplitAlign = 16;     // balanced: ranges and padded segments are multiples of this
-constexpr int kSegCost = 64;        // balanced: tokens' worth of per-item cost added per segment
 constexpr int kMinRange = 256;      // balanced: fewest tokens in a worker's range
 
 __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
@@ -64,7 +64,7 @@ __device__ __forceinline__ int64_t split_run(int ctx) {
     return ctx <= 0 ? kSplitAlign : ((int64_t)ctx + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
 }
 // length of a balanced segment in the range space
-__device__ __forceinline__ int64_t split_len(int ctx) { return split_run(ctx) + kSegCost; }
+__device__ __forceinline__ int64_t split_len(int ctx, int seg_cost) { return split_run(ctx) + seg_cost; }
 
 // balanced: tokens per worker range for T padded tokens over `grid` workers
 // x / y for 0 <= x and 0 < y, in 32 bits when both fit (the common case)
@@ -209,14 +209,14 @@ struct Schedule {
             for (int i = beg; i < end; ++i) {
                 const int c = clamp_ctx(a.ctx_lens[s0 + i], a.ctx_cap);
                 ctxw[i] = c;
-                own[0] += (uint64_t)split_len(c);
+                own[0] += (uint64_t)split_len(c, a.seg_cost);
             }
             uint64_t inc[1] = {own[0]};
             block_scan<NT, 1>(inc, tot);
             int64_t run = (int64_t)(inc[0] - own[0]);
             for (int i = beg; i < end; ++i) {
                 sp[i] = run;
-                run += split_len(ctxw[i]);
+                run += split_len(ctxw[i], a.seg_cost);
             }
             if (threadIdx.x == NT - 1) sp[n] = (int64_t)tot[0];
             spref = sp;
