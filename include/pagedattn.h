@@ -143,10 +143,12 @@ size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, in
  *                  of that many tokens, each partition produces (max, sum,
  *                  output) partials in `workspace`, and a log-sum-exp
  *                  reduction kernel merges them.
- *                  PA_PARTITION_BALANCED: the batch's contexts, laid end to
- *                  end, are cut into one equal token range per workgroup of
- *                  a launch that fills the GPU; contexts cut by a range
- *                  boundary are merged by the same log-sum-exp reduction.
+ *                  PA_PARTITION_BALANCED: the batch's contexts (each with a
+ *                  fixed per-item cost added), laid end to end, are cut into
+ *                  one equal range per wavefront of a launch that fills the
+ *                  GPU (a whole number per SIMD when the batch is small);
+ *                  contexts cut by a range boundary are merged by the same
+ *                  log-sum-exp reduction.
  *                  Every mode gives the single pass's result within rounding.
  *   workspace      DEVICE, >= pa_paged_attention_workspace_size(...) bytes,
  *                  256-byte aligned, no initial contents; may be NULL when
