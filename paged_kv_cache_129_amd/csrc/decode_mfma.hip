@@ -171,48 +171,74 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
     for (int s0 = 0; s0 < a.num_seqs; s0 += kWindow) {
         sch.build(a, s0, min(kWindow, a.num_seqs - s0), a.units, wl_lds, worker_id(wave, NW),
                   gridDim.x * NW, lane == 0);
+        // The query and the first block-table slice of an item are loaded while the
+        // previous item streams: `pre` holds them for the item in `itm`.
+        struct Prefetch {
+            TablePrefetch<64, WT> tbl;
+            Raw16 q[TILES][NC];
+        } pre;
+        auto prefetch = [&](const Item& it) {
+            const int kvh = it.unit / a.units_per_kv;
+            const int hg0 = (it.unit % a.units_per_kv) * a.unit_heads;
+            const int nh = min(a.unit_heads, G - hg0);
+            pre.tbl.issue(a.tables + (int64_t)it.s * a.max_blocks, it.t0 >> a.log2_bs,
+                          table_span(a, it.t0, it.t1, WT), a.max_blocks, lane);
+#pragma unroll
+            for (int tt = 0; tt < TILES; ++tt) {
+                const int hu = 16 * tt + c16;
+                const char* qrow = reinterpret_cast<const char*>(a.q) +
+                                   ((int64_t)it.s * a.num_heads + kvh * G + hg0 + (hu < nh ? hu : 0)) * D *
+                                       elem_bytes(QDT);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) pre.q[tt][c] = load16(qrow + dmap<KVDT, D>(c, j) * elem_bytes(QDT));
+            }
+        };
         Item itm;
-        while (sch.next(a, itm)) {
-            const int s = itm.s;
-            const int kvh = itm.unit / a.units_per_kv;
-            const int hg0 = (itm.unit % a.units_per_kv) * a.unit_heads;   // first head of the unit, within the group
+        bool have = sch.next(a, itm);
+        if (have) prefetch(itm);
+        while (have) {
+            // settle the prefetched loads (issued an item ago, or just now for the
+            // first item); the wait-count analysis cannot see across the item loop's
+            // back edge that they completed
+            __builtin_amdgcn_s_waitcnt(0);
+            const Item cur = itm;
+            const int s = cur.s;
+            const int kvh = cur.unit / a.units_per_kv;
+            const int hg0 = (cur.unit % a.units_per_kv) * a.unit_heads;   // first head of the unit, within the group
             const int nh = min(a.unit_heads, G - hg0);                   // heads of the unit
-            // first loads of the item, issued together: block-table segment, query
-            const int t0 = itm.t0, t1 = itm.t1;
+            const int t0 = cur.t0, t1 = cur.t1;
             const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
-            TablePrefetch<64, WT> tpre;
-            tpre.issue(trow, t0 >> a.log2_bs, table_span(a, t0, t1, WT), a.max_blocks, lane);
 
             // B operands of the score MFMA: Q^T[d][head] per 16-head tile, head = 16 tt + c16
             // of the unit (zero for padding heads)
             Op8 qop[TILES][NC];
 #pragma unroll
             for (int tt = 0; tt < TILES; ++tt) {
-                const int hu = 16 * tt + c16;
-                const bool live = hu < nh;
-                const char* qrow = reinterpret_cast<const char*>(a.q) +
-                                   ((int64_t)s * a.num_heads + kvh * G + hg0 + (live ? hu : 0)) * D *
-                                       elem_bytes(QDT);
+                const bool live = 16 * tt + c16 < nh;
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
-                    const int d = dmap<KVDT, D>(c, j);
                     Op8 o;
                     if constexpr (QDT == MT) {
-                        const Raw16 r = load16(qrow + d * 2);
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) o.w[q] = live ? r.w[q] : 0u;
+                        for (int q = 0; q < 4; ++q) o.w[q] = live ? pre.q[tt][c].w[q] : 0u;
                     } else {                       // bf16 query with an fp16 MFMA: widen then round
                         float f[8];
-                        unpack16<QDT>(load16(qrow + d * elem_bytes(QDT)), f);
+                        unpack16<QDT>(pre.q[tt][c], f);
 #pragma unroll
                         for (int q = 0; q < 4; ++q) o.w[q] = live ? pack_f16(f[2 * q], f[2 * q + 1]) : 0u;
                     }
                     qop[tt][c] = o;
                 }
             }
-            // settle the one-time loads here: the wait-count analysis cannot see across
-            // the token loop's back edge that they completed
-            __builtin_amdgcn_s_waitcnt(0);
+            // the first table slice, then the next item's loads, which stream in
+            // behind this item's
+            const int b_first = t0 >> a.log2_bs;
+            const int b_end = (t1 + bs - 1) >> a.log2_bs;
+            __builtin_amdgcn_wave_barrier();
+            pre.tbl.store(tbl, min(b_end, b_first + WT) - b_first, a.num_blocks, lane);
+            __builtin_amdgcn_wave_barrier();
+            have = sch.next(a, itm);
+            if (have) prefetch(itm);
 
             float m[TILES], l[TILES];
             f32x4 acc[TILES][NDT];
@@ -224,20 +250,16 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
                 for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
 
-            const int b_first = t0 >> a.log2_bs;
-            const int b_end = (t1 + bs - 1) >> a.log2_bs;
             for (int sb = b_first; sb < b_end; sb += WT) {
                 const int se = min(b_end, sb + WT);
-                __builtin_amdgcn_wave_barrier();
-                if (sb == b_first) {
-                    tpre.store(tbl, se - sb, a.num_blocks, lane);
-                } else {
+                if (sb != b_first) {             // later slices of a long item
+                    __builtin_amdgcn_wave_barrier();
                     for (int i = lane; i < se - sb; i += 64) {
                         const int b = trow[sb + i];
                         tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
                     }
+                    __builtin_amdgcn_wave_barrier();
                 }
-                __builtin_amdgcn_wave_barrier();
                 const int ts = max(t0, sb << a.log2_bs);
                 const int te = min(t1, se << a.log2_bs);
 
@@ -463,15 +485,15 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
                 if (hu < nh) {
                     const int head = kvh * G + hg0 + hu;
                     const float inv_l = lt > 0.0f ? 1.0f / lt : 0.0f;
-                    const int64_t r = itm.rec0 + (int64_t)hu * itm.rec_stride;
-                    if (!itm.whole && j == 0) {
+                    const int64_t r = cur.rec0 + (int64_t)hu * cur.rec_stride;
+                    if (!cur.whole && j == 0) {
                         a.ws[r] = m[tt];
                         a.ws[a.nrec + r] = lt;
                     }
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
                         const int d = 16 * dt + 4 * j;
-                        if (itm.whole) {
+                        if (cur.whole) {
                             const float f = inv_l * a.out_scale;
                             char* op = reinterpret_cast<char*>(a.out) +
                                        (((int64_t)s * a.num_heads + head) * D + d) * elem_bytes(QDT);
