@@ -356,7 +356,7 @@ def main():
                          "HBM counters can be scaled by a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         sys.exit(2)
 
