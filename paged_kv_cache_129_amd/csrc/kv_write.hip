@@ -22,21 +22,23 @@ __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t i = idx / per_token;
     if (i >= a.num_tokens) return;
+    const int64_t e = (idx - i * per_token) * VEC;     // element within the token row
+    const int64_t src = i * a.num_kv_heads * a.head_dim + e;
+    // the new values do not depend on the slot: load them together with it
+    const Raw16 rk = load16(reinterpret_cast<const char*>(a.k_new) + src * SB);
+    const Raw16 rv = load16(reinterpret_cast<const char*>(a.v_new) + src * SB);
     const int64_t slot = a.slot_mapping[i];
     if (slot < 0 || slot >= a.num_slots) return;       // -1 (or out of range): no token
-    const int64_t e = (idx - i * per_token) * VEC;     // element within the token row
     const int64_t head = e / a.head_dim;
     const int64_t d = e - head * a.head_dim;
     const int64_t blk = slot >> a.log2_bs;
     const int64_t off = slot & ((1 << a.log2_bs) - 1);
     const int64_t dst = (((blk * a.num_kv_heads + head) << a.log2_bs) + off) * a.head_dim + d;
-    const int64_t src = i * a.num_kv_heads * a.head_dim + e;
 
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv) {
-        const char* s = reinterpret_cast<const char*>(kv ? a.v_new : a.k_new) + src * SB;
         char* p = reinterpret_cast<char*>(kv ? a.v_pool : a.k_pool) + dst * DB;
-        const Raw16 r = load16(s);
+        const Raw16 r = kv ? rv : rk;
         if constexpr (SRC == KV) {
             store16(p, r);
         } else {
