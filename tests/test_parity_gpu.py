@@ -469,3 +469,79 @@ def test_score_drift(kv, q, H, Hkv, drift):
                               context_lens=ctx, kv_dtype=kv, q_dtype=q, spare_blocks=3,
                               salt=H, key_drift=drift)
     run_and_check(case, partitions=(0, -1, 64))
+
+
+# ------------------------------------------------------------------ shared prompts
+# Tables in which sequences reference their predecessor's first blocks (the
+# parallel samples of one prompt after a fork), in every launch mode: runs of
+# sharing sequences of several lengths, sharing that breaks off along a run,
+# long shared prefixes, small and large blocks, sequences cut across workers
+# of the balanced split, runs across the schedule's 1024-sequence windows.
+# The oracle reads every sequence through its own table.
+def _share(case, groups):
+    """groups: (first sequence, sequences, shared blocks) — the later sequences'
+    first table entries are made the first one's."""
+    t = case.block_tables
+    bs = case.block_size
+    for lead, n, k in groups:
+        for j in range(lead + 1, lead + n):
+            assert k * bs <= min(case.context_lens[j], case.context_lens[lead])
+            t[j, :k] = t[lead, :k]
+    return case
+
+
+SHARE_CASES = [
+    # name, kv, q, D, bs, H, Hkv, ctx, groups (first, sequences, shared blocks)
+    ("g8_pairs", "bf16", "bf16", 128, 16, 64, 8,
+     [521, 530, 600, 512, 300, 330, 400, 321, 90, 1, 17, 700],
+     [(0, 4, 32), (5, 3, 20)]),
+    ("g4_six_empty_tail", "f16", "f16", 128, 32, 16, 4,
+     [320, 321, 350, 370, 330, 400, 5], [(0, 6, 10)]),
+    ("g2_nine_fp8", "fp8_e4m3", "f16", 64, 8, 4, 2,
+     [330, 331, 340, 360, 333, 350, 420, 336, 400, 44], [(0, 9, 40)]),
+    ("g8_broken_chain", "bf16", "bf16", 128, 16, 16, 2,
+     [400, 410, 420, 430, 300, 500], [(0, 2, 20), (1, 2, 10), (2, 2, 18), (4, 2, 16)]),
+    ("g4_long_prefix", "f16", "f16", 64, 16, 8, 2,
+     [2500, 2410, 1030, 1040, 1024, 1050, 1100, 1045], [(0, 2, 150), (2, 2, 64), (4, 2, 64), (6, 2, 65)]),
+    ("g8_bs64_and_bs4", "bf16", "bf16", 128, 64, 16, 2, [600, 640, 700, 20], [(0, 3, 9)]),
+    ("g4_bs4", "f16", "f16", 128, 4, 8, 2, [270, 290, 300, 260, 3], [(0, 4, 65)]),
+    ("g8_fp8_q_bf16", "fp8_e4m3", "bf16", 128, 16, 16, 2, [700, 720, 650, 2], [(0, 3, 40)]),
+]
+
+
+@pytest.mark.parametrize("name,kv,q,D,bs,H,Hkv,ctx,groups", SHARE_CASES,
+                         ids=[c[0] for c in SHARE_CASES])
+def test_shared_prompt_groups(name, kv, q, D, bs, H, Hkv, ctx, groups):
+    case = W.make_decode_case(f"share_{name}", "tiny", num_seqs=len(ctx), num_heads=H,
+                              num_kv_heads=Hkv, head_dim=D, block_size=bs, context_lens=ctx,
+                              kv_dtype=kv, q_dtype=q, spare_blocks=5, append=False, salt=len(name))
+    run_and_check(_share(case, groups), partitions=(-1, 0, 64))
+
+
+def test_shared_prompt_groups_cut_across_workers():
+    """Enough work that balanced ranges are a few hundred tokens, so sharing
+    sequences are cut across several workers and merged."""
+    rng = np.random.default_rng(11)
+    ctx, groups = [], []
+    for g in range(12):
+        lead = len(ctx)
+        shared = int(rng.integers(20, 60))
+        n = int(rng.integers(2, 6))
+        ctx += [shared * 16 + int(rng.integers(0, 300)) for _ in range(n)]
+        groups.append((lead, n, shared))
+        ctx.append(int(rng.integers(1, 1500)))             # an unrelated sequence between groups
+    case = W.make_decode_case("share_cut", "tiny", num_seqs=len(ctx), num_heads=64, num_kv_heads=8,
+                              head_dim=128, block_size=16, context_lens=ctx, kv_dtype="bf16",
+                              q_dtype="bf16", spare_blocks=5, append=False, salt=3)
+    run_and_check(_share(case, groups), partitions=(-1, 0))
+
+
+def test_shared_prompt_groups_at_window_edges():
+    """Runs of sharing sequences across the schedule's 1024-sequence window boundary."""
+    ctx = [int(x) for x in np.random.default_rng(5).integers(0, 40, size=1100)]
+    for i in list(range(1018, 1030)) + [0, 1, 2, 1098, 1099]:
+        ctx[i] = 300 + (i % 7) * 10
+    case = W.make_decode_case("share_windows", "tiny", num_seqs=len(ctx), num_heads=8,
+                              num_kv_heads=2, head_dim=64, block_size=16, context_lens=ctx,
+                              kv_dtype="f16", q_dtype="f16", spare_blocks=5, append=False, salt=9)
+    run_and_check(_share(case, [(1018, 12, 18), (0, 3, 17), (1098, 2, 16)]), partitions=(-1, 0))
