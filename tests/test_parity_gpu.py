@@ -545,3 +545,16 @@ def test_shared_prompt_groups_at_window_edges():
                               num_kv_heads=2, head_dim=64, block_size=16, context_lens=ctx,
                               kv_dtype="f16", q_dtype="f16", spare_blocks=5, append=False, salt=9)
     run_and_check(_share(case, [(1018, 12, 18), (0, 3, 17), (1098, 2, 16)]), partitions=(-1, 0))
+
+
+# ------------------------------------------------------------------ item transitions
+# Few tokens per worker, so every worker streams many items back to back, with
+# empty contexts (items with no tokens) and one-chunk items between longer ones.
+@pytest.mark.parametrize("kv,q,H,Hkv,bs", [("bf16", "bf16", 64, 8, 16), ("fp8_e4m3", "f16", 8, 4, 32),
+                                           ("f16", "f16", 71, 1, 16), ("f16", "f16", 16, 2, 64)])
+def test_item_transitions_with_empty_contexts(kv, q, H, Hkv, bs):
+    ctx = [0, 5, 0, 0, 40, 0, 16, 17, 0, 300, 33, 0, 1, 64, 0, 0, 129, 2, 0, 31] * 3
+    case = W.make_decode_case(f"transitions_{kv}_{H}_{bs}", "tiny", num_seqs=len(ctx), num_heads=H,
+                              num_kv_heads=Hkv, head_dim=128 if H != 71 else 64, block_size=bs,
+                              context_lens=ctx, kv_dtype=kv, q_dtype=q, spare_blocks=3, salt=bs + H)
+    run_and_check(case, partitions=(-1, 0, 16))
