@@ -142,7 +142,11 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
     constexpr int EB = elem_bytes(KVDT);
     constexpr int NC = D / 32;               // score MFMAs per chunk and tile
     constexpr int NDT = D / 16;              // output d-tiles
-    constexpr int LDV = D + 8;               // LDS row stride of a staged V tile (halfs)
+    // LDS row stride of a staged V tile (halfs).  16-bit caches: D + 16 puts the
+    // eight rows a 32-lane pass of the transposed read touches 8 banks apart (no
+    // bank conflicts; D + 8 had 2-way ones on a quarter of the LDS cycles).  fp8
+    // caches write 32 widened bytes per lane, which conflict less with D + 8.
+    constexpr int LDV = KVDT == PA_FP8_E4M3 ? D + 8 : D + 16;
     constexpr int PPR = D * EB / 16;         // 16-byte pieces per V row
     constexpr int NPV = kChunk * PPR / 64;   // V pieces per lane per chunk
     constexpr int VEL = 16 / EB;             // numbers per V piece
