@@ -335,6 +335,29 @@ def calibrate_copy(pa, torch, mib):
 
 
 # ---------------------------------------------------------------- main
+def reference_copy_gbs(torch, mib=512, reps=10):
+    """Device-to-device copy of `mib` MiB with the runtime's copy (read + write bytes
+    per second): the bandwidth a plain streaming kernel reaches on this device,
+    shown beside the 8 TB/s denominator.  Measured before the workload's pools
+    are allocated, and freed again."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * n * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -370,6 +393,8 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy_mib > 0:
         calibrate_copy(pa, torch, args.calibrate_copy_mib)
+    copy_gbs = reference_copy_gbs(torch)
+    log(f"reference device-to-device copy: {copy_gbs:.0f} GB/s (read + write)")
     if args.partition_size is None:
         args.partition_size = DEFAULT_PARTITION[args.workload]
     wl = WORKLOADS[args.workload](pa, W, torch, args.partition_size, args)
@@ -412,6 +437,17 @@ def main():
     decode_ms = start.elapsed_time(end) / (rounds * wl.L)
     achieved = wl.attn_bytes / (decode_ms * 1e-3) / 1e9
     log(f"decode attention: {decode_ms * 1e3:.1f} us per launch, {achieved:.0f} GB/s")
+    # spread of single calls (eager, each between its own events on the launch stream)
+    singles = []
+    for i in range(max(10, min(60, args.decode_iters))):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        wl.decode(i % wl.L)
+        b.record()
+        b.synchronize()
+        singles.append(a.elapsed_time(b) * 1e3)
+    p10, p50, p90 = (float(np.percentile(singles, q)) for q in (10, 50, 90))
+    log(f"single calls: p10 {p10:.1f} p50 {p50:.1f} p90 {p90:.1f} us")
 
     value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
     traffic, traffic_src = read_traffic(args.workload, args.partition_size)
@@ -435,8 +471,10 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "paged_attention_decode",
                      "avg_launch_us": round(decode_ms * 1e3, 2),
+                     "single_call_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
                      "algorithmic_bytes_per_launch": wl.attn_bytes,
-                     "traffic_source": traffic_src},
+                     "traffic_source": traffic_src,
+                     "reference_copy_gbs": round(copy_gbs, 1)},
         "cpu_baseline": None,
     }
 
