@@ -276,17 +276,38 @@ template <int QDT, int D>
 __global__ __launch_bounds__(256) void split_reduce_kernel(DecodeArgs a) {
     constexpr int LPH = D / 16;                 // lanes per head
     constexpr int HP = 64 / LPH;                // heads per pass
-    constexpr int B = 8;                        // records per batch
+    constexpr int B = 4;                        // records per batch
     const int64_t windows = (a.num_seqs + kWindow - 1) / kWindow;
     const int GR = a.unit_heads;                        // record slots per unit
     const int lane = threadIdx.x & 63;
     const int hl = lane / LPH, d0 = (lane % LPH) * 16;
     const int64_t wb = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
     if (wb >= windows * a.workers) return;
+    const int64_t win = wb / a.workers, b = wb % a.workers;
+    // The common case, a segment cut once that started inside worker b - 1's range, has
+    // its pieces in slot 1 of worker b - 1 and slot 0 of worker b: their records for
+    // the first SP passes are loaded together with the descriptor (in bounds whatever
+    // the descriptor says; used only in that case).
+    constexpr int SP = D == 64 ? 2 : 1;
+    float smv[SP][2], slv[SP][2];
+    float4 sov[SP][2][4];
+#pragma unroll
+    for (int p = 0; p < SP; ++p) {
+        const int isp = min(p * HP + hl, GR - 1);
+        const int64_t rs[2] = {((win * a.workers + (b > 0 ? b - 1 : b)) * 2 + 1) * GR + isp,
+                               ((win * a.workers + b) * 2 + 0) * GR + isp};
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            smv[p][q] = a.ws[rs[q]];
+            slv[p][q] = a.ws[a.nrec + rs[q]];
+            const float4* op = reinterpret_cast<const float4*>(a.ws + 2 * a.nrec + rs[q] * D + d0);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) sov[p][q][v] = op[v];
+        }
+    }
     const int64_t* d = a.desc + wb * kDescWords;
     const int64_t t0 = d[1], range = d[3];
     const int64_t run = split_run((int)d[4]);
-    const int64_t win = wb / a.workers, b = wb % a.workers;
     if (t0 <= 0 || t0 >= run) return;                   // no cut tokens end in this range
     const int64_t start = b * range - t0;               // the segment's first token, range space
     if (start + run > (b + 1) * range) return;          // a later range holds the last piece
@@ -297,7 +318,9 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(DecodeArgs a) {
     const int hg0 = (unit % a.units_per_kv) * GR;
     const int nh = min(GR, Gq - hg0);                   // heads of the unit
     const int64_t head0 = (int64_t)(unit / a.units_per_kv) * Gq + hg0;
-    for (int h0 = 0; h0 < nh; h0 += HP) {
+    for (int pass = 0; pass < (GR + HP - 1) / HP; ++pass) {
+        const int h0 = pass * HP;
+        if (h0 >= nh) break;
         const int i = min(h0 + hl, nh - 1);             // lanes past the unit repeat its last head
         auto rec = [&](int k) -> int64_t {
             const int64_t w = first + k;
@@ -306,34 +329,49 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(DecodeArgs a) {
         float M = kNegInf, den = 0.0f, num[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) num[e] = 0.0f;
-        for (int k0 = 0; k0 < n; k0 += B) {
-            float mv[B], lv[B];
-            float4 ov[B][4];
+        // online merge of one piece's record (pieces in range order)
+        auto take = [&](float mq, float lq, const float4* oq) {
+            if (mq != kNegInf) {
+                const float Mn = fmaxf(M, mq);
+                const float sc = (M == kNegInf) ? 0.0f : fast_exp2(M - Mn);
+                const float w = fast_exp2(mq - Mn) * lq;
+                den = den * sc + w;
 #pragma unroll
-            for (int q = 0; q < B; ++q) {
-                const int64_t r = rec(min(k0 + q, n - 1));
-                mv[q] = a.ws[r];
-                lv[q] = a.ws[a.nrec + r];
-                const float4* op = reinterpret_cast<const float4*>(a.ws + 2 * a.nrec + r * D + d0);
-#pragma unroll
-                for (int v = 0; v < 4; ++v) ov[q][v] = op[v];
-            }
-#pragma unroll
-            for (int q = 0; q < B; ++q) {
-                if (k0 + q < n && mv[q] != kNegInf) {
-                    const float Mn = fmaxf(M, mv[q]);
-                    const float sc = (M == kNegInf) ? 0.0f : fast_exp2(M - Mn);
-                    const float w = fast_exp2(mv[q] - Mn) * lv[q];
-                    den = den * sc + w;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        num[4 * v + 0] = num[4 * v + 0] * sc + w * ov[q][v].x;
-                        num[4 * v + 1] = num[4 * v + 1] * sc + w * ov[q][v].y;
-                        num[4 * v + 2] = num[4 * v + 2] * sc + w * ov[q][v].z;
-                        num[4 * v + 3] = num[4 * v + 3] * sc + w * ov[q][v].w;
-                    }
-                    M = Mn;
+                for (int v = 0; v < 4; ++v) {
+                    num[4 * v + 0] = num[4 * v + 0] * sc + w * oq[v].x;
+                    num[4 * v + 1] = num[4 * v + 1] * sc + w * oq[v].y;
+                    num[4 * v + 2] = num[4 * v + 2] * sc + w * oq[v].z;
+                    num[4 * v + 3] = num[4 * v + 3] * sc + w * oq[v].w;
                 }
+                M = Mn;
+            }
+        };
+        bool done = false;
+#pragma unroll
+        for (int p = 0; p < SP; ++p) {
+            if (p == pass && n == 2 && t0 < range) {    // the records loaded up front (a segment
+                                                        // starting a range keeps its slot 0 there)
+                take(smv[p][0], slv[p][0], sov[p][0]);
+                take(smv[p][1], slv[p][1], sov[p][1]);
+                done = true;
+            }
+        }
+        if (!done) {
+            for (int k0 = 0; k0 < n; k0 += B) {
+                float mv[B], lv[B];
+                float4 ov[B][4];
+#pragma unroll
+                for (int q = 0; q < B; ++q) {
+                    const int64_t r = rec(min(k0 + q, n - 1));
+                    mv[q] = a.ws[r];
+                    lv[q] = a.ws[a.nrec + r];
+                    const float4* op = reinterpret_cast<const float4*>(a.ws + 2 * a.nrec + r * D + d0);
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) ov[q][v] = op[v];
+                }
+#pragma unroll
+                for (int q = 0; q < B; ++q)
+                    if (k0 + q < n) take(mv[q], lv[q], ov[q]);
             }
         }
         if (h0 + hl < nh) {
