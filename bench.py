@@ -294,9 +294,10 @@ WORKLOADS = {"llama7b": Llama7B, "opt13b": Opt13B, "falcon7b": Falcon7B, "llama7
              "tiny": Tiny}
 
 
-def read_traffic(workload, partition_size):
+def read_traffic(workload, partition_size, block_size):
     """HBM traffic per launch of the dominant kernel from the committed counter
-    summary, if the kernel sources are unchanged since the counters were taken."""
+    summary of the same workload, launch mode and block size, if the kernel
+    sources are unchanged since the counters were taken."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.traffic.txt"))):
@@ -307,7 +308,8 @@ def read_traffic(workload, partition_size):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
         if kv.get("workload") != workload or "partition_size" not in kv or \
-                int(kv["partition_size"]) != partition_size:
+                int(kv["partition_size"]) != partition_size or \
+                int(kv.get("block_size", "0")) != block_size:
             continue
         h = hashlib.sha256()
         try:
@@ -450,7 +452,7 @@ def main():
     log(f"single calls: p10 {p10:.1f} p50 {p50:.1f} p90 {p90:.1f} us")
 
     value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
-    traffic, traffic_src = read_traffic(args.workload, args.partition_size)
+    traffic, traffic_src = read_traffic(args.workload, args.partition_size, wl.bs)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
