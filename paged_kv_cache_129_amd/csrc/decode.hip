@@ -269,7 +269,7 @@ __global__ __launch_bounds__(64) void lse_reduce_kernel(DecodeArgs a) {
 // the pieces are held by workers first..b (first: slot 1 unless its range
 // starts exactly at the segment, every other one: slot 0).  One wavefront per
 // worker: it reads the worker's descriptor and, if the worker holds such a
-// last piece, merges all heads of the segment's unit, kSplitHeads heads per
+// last piece, merges all heads of the segment's unit, 64 / (D / 16) heads per
 // pass with 16 consecutive dimensions of one head per lane (so every record
 // is fetched in 16-byte pieces, all records of a batch at once).
 template <int QDT, int D>
