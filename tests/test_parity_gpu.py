@@ -558,3 +558,34 @@ def test_item_transitions_with_empty_contexts(kv, q, H, Hkv, bs):
                               num_kv_heads=Hkv, head_dim=128 if H != 71 else 64, block_size=bs,
                               context_lens=ctx, kv_dtype=kv, q_dtype=q, spare_blocks=3, salt=bs + H)
     run_and_check(case, partitions=(-1, 0, 16))
+
+
+# ------------------------------------------------------------------ seeded random configurations
+def _random_config(seed):
+    r = np.random.default_rng(1000 + seed)
+    kv, q = [("f32", "f32"), ("f16", "f16"), ("bf16", "bf16"), ("fp8_e4m3", "f16"),
+             ("fp8_e4m3", "bf16"), ("fp8_e4m3", "f32")][int(r.integers(0, 6))]
+    D = int(r.choice([64, 128]))
+    Hkv = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 2, 3, 4, 5, 8, 16, 20, 33, 71]))
+    bs = int(r.choice([1, 2, 4, 8, 16, 32, 64, 128, 256]))
+    S = int(r.integers(1, 24))
+    mix = int(r.integers(0, 3))
+    if mix == 0:                       # short and empty contexts
+        ctx = r.integers(0, 40, size=S)
+    elif mix == 1:                     # one long context among short ones
+        ctx = r.integers(1, 200, size=S)
+        ctx[int(r.integers(0, S))] = int(r.integers(1500, 5000))
+    else:                              # log-normal
+        ctx = np.clip(np.rint(np.exp(r.normal(np.log(300), 0.8, size=S))), 1, 3000)
+    return kv, q, D, bs, G * Hkv, Hkv, [int(c) for c in ctx]
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_configurations(seed):
+    kv, q, D, bs, H, Hkv, ctx = _random_config(seed)
+    case = W.make_decode_case(f"random_{seed}", "tiny", num_seqs=len(ctx), num_heads=H,
+                              num_kv_heads=Hkv, head_dim=D, block_size=bs, context_lens=ctx,
+                              kv_dtype=kv, q_dtype=q, spare_blocks=int(seed % 5), salt=seed,
+                              max_blocks=int(W.blocks_needed(ctx, bs).max()) + 1 + seed % 3)
+    run_and_check(case, partitions=(0, -1, max(bs, 64 // bs * bs), 512))
