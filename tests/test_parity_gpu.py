@@ -111,6 +111,79 @@ def test_llama70b_gqa_shared_prompt_cow(full):
         assert err <= TOL["bf16"]
 
 
+def _graph_step_case(kind):
+    if kind == "gqa_cow_bf16":
+        spec = W.SharedPromptSpec(independent_ctx=W.llama70b_independent_lengths(6)[:6] - 1,
+                                  groups=2, samples=3, prompt_len=300)
+        return _llama70b(spec, 4096)
+    ctx = [0, 1, 17, 300, 700, 64, 129]
+    case = W.make_decode_case("graph_mqa_fp8", "tiny", num_seqs=len(ctx), num_heads=71,
+                              num_kv_heads=1, head_dim=64, block_size=16, context_lens=ctx,
+                              kv_dtype="fp8_e4m3", q_dtype="f16", spare_blocks=8)
+    return case, np.zeros((0, 2), dtype=np.int32)
+
+
+@pytest.mark.parametrize("ps", [0, 512, pa.PARTITION_BALANCED])
+@pytest.mark.parametrize("kind", ["gqa_cow_bf16", "mqa_fp8"])
+def test_whole_step_graph_replays(kind, ps):
+    """One decode step (copy-on-write block copies, cache write, attention)
+    captured as one HIP graph and replayed several times; between replays the
+    pools are put back to their pre-step bytes eagerly.  Every replay's pools
+    match the oracle bit for bit and its output matches the oracle's attention
+    and the eager step's output exactly."""
+    case, pairs = _graph_step_case(kind)
+    say(f"[case] whole-step graph {kind} partition={ps} S={case.num_seqs} pairs={len(pairs)}")
+    kp, vp = case.k_pool.copy(), case.v_pool.copy()
+    if len(pairs):
+        oracle.copy_blocks([kp, vp], [tuple(p) for p in pairs])
+    oracle.kv_write(kp, vp, case.kv_dtype, case.k_new, case.v_new, case.q_dtype,
+                    case.slot_mapping, case.block_size, case.k_scale, case.v_scale)
+    ref = oracle.paged_attention(case.q, case.q_dtype, kp, vp, case.kv_dtype, case.block_tables,
+                                 case.context_lens, case.block_size, case.scale, case.k_scale,
+                                 case.v_scale)
+    dev = DeviceCase(case)
+    k0, v0 = dev.k_pool.clone(), dev.v_pool.clone()
+    need = pa.paged_attention_workspace_size(case.num_seqs, case.num_heads, case.num_kv_heads,
+                                             case.head_dim, case.max_context_len, ps)
+    ws = pa.new_workspace(need, "cuda")
+    out = torch.full_like(dev.q, float("nan"))
+
+    def step():
+        if len(pairs):
+            pa.copy_blocks([dev.k_pool], [dev.v_pool], pairs)
+        dev.write()
+        pa.paged_attention_decode(out, dev.q, dev.k_pool, dev.v_pool, dev.tables, dev.ctx,
+                                  max_context_len=case.max_context_len, scale=case.scale,
+                                  k_scale=case.k_scale, v_scale=case.v_scale,
+                                  partition_size=ps, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    assert_pools_equal(dev, kp, vp)
+    eager = out_to_f64(out)
+    assert max_err(eager, ref, case.q_dtype) <= TOL[case.kv_dtype]
+    dev.k_pool.copy_(k0)
+    dev.v_pool.copy_(v0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        dev.k_pool.copy_(k0)
+        dev.v_pool.copy_(v0)
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_pools_equal(dev, kp, vp)
+        got = out_to_f64(out)
+        err = max_err(got, ref, case.q_dtype)
+        say(f"    replay {rep}: max-abs error {err:.3g}")
+        assert err <= TOL[case.kv_dtype]
+        assert np.array_equal(got, eager), "replay differs from the eager step"
+    del g
+
+
 def test_llama7b_full_size_sampled():
     """64 sequences at context 4096, 17,408-block pool (4 GiB per layer): GPU writes
     and attends over the whole batch; the oracle recomputes sampled sequences from
