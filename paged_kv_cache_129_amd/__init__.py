@@ -133,6 +133,20 @@ def _dev(t, name: str):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _same_dtype(a, b, na: str, nb: str):
+    """K and V operands are read with one element type: a narrower one would be
+    read past its end."""
+    if a.dtype != b.dtype:
+        raise ValueError(f"{na} and {nb} differ in dtype ({a.dtype} vs {b.dtype})")
+
+
+def _one_device(*tensors):
+    dev = tensors[0].device
+    for t in tensors[1:]:
+        if t.device != dev:
+            raise ValueError(f"tensors on different devices ({dev} and {t.device})")
+
+
 def _stream(stream, device):
     torch = _torch()
     if stream is None:
@@ -150,6 +164,9 @@ def kv_cache_write(k_new, v_new, k_pool, v_pool, slot_mapping, *, k_scale: float
         raise ValueError("shape mismatch")
     if slot_mapping.dtype != _torch().int64 or slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be int64 [T]")
+    _same_dtype(k_new, v_new, "k_new", "v_new")
+    _same_dtype(k_pool, v_pool, "k_pool", "v_pool")
+    _one_device(k_new, v_new, k_pool, v_pool, slot_mapping)
     _check(lib.pa_kv_cache_write(_dev(k_new, "k_new"), _dev(v_new, "v_new"), dtype_code(k_new),
                                  _dev(k_pool, "k_pool"), _dev(v_pool, "v_pool"),
                                  dtype_code(k_pool), _dev(slot_mapping, "slot_mapping"), T, Hkv, D,
@@ -186,6 +203,9 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, *
         raise ValueError("block_tables must be int32 [S, max_blocks]")
     if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
         raise ValueError("context_lens must be int32 [S]")
+    _same_dtype(k_pool, v_pool, "k_pool", "v_pool")
+    _one_device(out, q, k_pool, v_pool, block_tables, context_lens,
+                *([workspace] if workspace is not None else []))
     need = paged_attention_workspace_size(S, H, Hkv, D, max_context_len, partition_size)
     if need and workspace is None:
         workspace = new_workspace(need, q.device)
@@ -211,6 +231,7 @@ def copy_blocks(k_pools: Sequence, v_pools: Sequence, pairs, *, stream=None) -> 
     for p in list(k_pools) + list(v_pools):
         if p.shape != k_pools[0].shape or p.dtype != k_pools[0].dtype:
             raise ValueError("all pools must share shape and dtype")
+    _one_device(*k_pools, *v_pools)
     kp = (ctypes.c_void_p * L)(*[_dev(p, "k_pool").value for p in k_pools])
     vp = (ctypes.c_void_p * L)(*[_dev(p, "v_pool").value for p in v_pools])
     _check(lib.pa_copy_blocks(kp, vp, L, dtype_code(k_pools[0]), Hkv, D, bs, NB,

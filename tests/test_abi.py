@@ -159,3 +159,47 @@ def test_copy_noop_and_null_pool():
     assert copy_call([], n=0) == 0
     kp = (ctypes.c_void_p * 2)(0x1000, 0)
     assert copy_call([(1, 2)], k=kp) == -1
+
+
+# ------------------------------------------------------------------ binding checks (host only)
+def _binding_tensors(kv_v_dtype, device_v="cpu"):
+    import torch
+    q = torch.zeros(2, 4, 64, dtype=torch.float16)
+    kp = torch.zeros(8, 2, 16, 64, dtype=torch.float16)
+    vp = torch.zeros(8, 2, 16, 64, dtype=kv_v_dtype, device=device_v)
+    tables = torch.zeros(2, 4, dtype=torch.int32)
+    ctx = torch.ones(2, dtype=torch.int32)
+    return q, kp, vp, tables, ctx
+
+
+def test_binding_rejects_kv_pools_of_different_dtypes():
+    """A V pool of a narrower type than K's would be read past its end."""
+    import torch
+    q, kp, vp, tables, ctx = _binding_tensors(torch.uint8)
+    with pytest.raises(ValueError, match="differ in dtype"):
+        pa.paged_attention_decode(torch.empty_like(q), q, kp, vp, tables, ctx,
+                                  max_context_len=64, scale=0.125)
+    k_new = torch.zeros(2, 2, 64, dtype=torch.float16)
+    slots = torch.zeros(2, dtype=torch.int64)
+    with pytest.raises(ValueError, match="differ in dtype"):
+        pa.kv_cache_write(k_new, k_new.to(torch.bfloat16), kp, kp.clone(), slots)
+    with pytest.raises(ValueError, match="differ in dtype"):
+        pa.kv_cache_write(k_new, k_new, kp, vp, slots)
+
+
+def test_binding_rejects_tensors_on_different_devices():
+    import torch
+    q, kp, vp, tables, ctx = _binding_tensors(torch.float16, device_v="meta")
+    with pytest.raises(ValueError, match="different devices"):
+        pa.paged_attention_decode(torch.empty_like(q), q, kp, vp, tables, ctx,
+                                  max_context_len=64, scale=0.125)
+    with pytest.raises(ValueError, match="different devices"):
+        pa.copy_blocks([kp], [vp], [(0, 1)])
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+    q, kp, vp, tables, ctx = _binding_tensors(torch.float16)
+    with pytest.raises(ValueError, match="device tensor"):
+        pa.paged_attention_decode(torch.empty_like(q), q, kp, vp, tables, ctx,
+                                  max_context_len=64, scale=0.125)
