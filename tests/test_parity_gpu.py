@@ -184,6 +184,72 @@ def test_whole_step_graph_replays(kind, ps):
     del g
 
 
+@pytest.mark.parametrize("kv,q,H,Hkv", [("f16", "f16", 8, 8), ("bf16", "bf16", 64, 8),
+                                        ("fp8_e4m3", "bf16", 32, 4)])
+def test_pools_beyond_4gib(kv, q, H, Hkv):
+    """Pools of about 4.5 GiB each, the case's blocks placed at ids whose byte
+    offsets straddle 2 GiB and 4 GiB and at the pool's last block: cache write,
+    block copy and attention address them with 64-bit offsets.  Outputs do not
+    depend on placement, so the oracle runs on the compact case."""
+    ctx = [1, 33, 700, 1500, 16, 0, 2049]
+    case = W.make_decode_case(f"big_{kv}_{H}", "tiny", num_seqs=len(ctx), num_heads=H,
+                              num_kv_heads=Hkv, head_dim=128, block_size=16, context_lens=ctx,
+                              kv_dtype=kv, q_dtype=q, spare_blocks=2, salt=H)
+    kp, vp, ref = oracle_step(case)
+    nb = case.k_pool.shape[0]
+    block_bytes = Hkv * 16 * 128 * (1 if kv == "fp8_e4m3" else 2)
+    NB = (9 << 29) // block_bytes + 2                      # 4.5 GiB and two blocks
+    b2, b4 = (1 << 31) // block_bytes, (1 << 32) // block_bytes
+    forced = [b2 - 1, b2, b4 - 1, b4, NB - 2, NB - 1]
+    rng = np.random.default_rng(nb)
+    rest = rng.choice(np.setdiff1d(np.arange(NB - 2), forced), size=nb - len(forced) + 1,
+                      replace=False)
+    remap = np.concatenate([forced, rest]).astype(np.int64)
+    spare = int(remap[-1])                                  # a block no table uses
+    remap = remap[:nb]
+    rng.shuffle(remap)
+    say(f"[case] pools beyond 4 GiB kv={kv} H={H} Hkv={Hkv} NB={NB} "
+        f"({NB * block_bytes / 2**30:.2f} GiB per pool)")
+    small = DeviceCase(case)
+    tdt = small.k_pool.dtype
+    idx = torch.from_numpy(remap).cuda()
+    big_k = torch.empty((NB, Hkv, 16, 128), dtype=tdt, device="cuda")
+    big_v = torch.empty_like(big_k)
+    big_k[idx] = small.k_pool
+    big_v[idx] = small.v_pool
+    tables = np.where(case.block_tables >= 0, remap[np.maximum(case.block_tables, 0)], -1)
+    slots = np.where(case.slot_mapping >= 0,
+                     remap[np.maximum(case.slot_mapping, 0) // 16] * 16 + case.slot_mapping % 16,
+                     -1)
+    tables_d = torch.from_numpy(tables.astype(np.int32)).cuda()
+    pa.kv_cache_write(small.k_new, small.v_new, big_k, big_v,
+                      torch.from_numpy(slots.astype(np.int64)).cuda(),
+                      k_scale=case.k_scale, v_scale=case.v_scale)
+    torch.cuda.synchronize()
+    gk, gv = from_dev(big_k[idx], kv), from_dev(big_v[idx], kv)
+    assert np.array_equal(W.raw_view(gk, kv), W.raw_view(kp, kv)), "K pool differs after write"
+    assert np.array_equal(W.raw_view(gv, kv), W.raw_view(vp, kv)), "V pool differs after write"
+    for ps in (0, pa.PARTITION_BALANCED, 512):
+        out = torch.full_like(small.q, float("nan"))
+        pa.paged_attention_decode(out, small.q, big_k, big_v, tables_d, small.ctx,
+                                  max_context_len=case.max_context_len, scale=case.scale,
+                                  k_scale=case.k_scale, v_scale=case.v_scale, partition_size=ps)
+        torch.cuda.synchronize()
+        err = max_err(out_to_f64(out), ref, q)
+        say(f"    partition {ps}: max-abs error {err:.3g}")
+        assert err <= TOL[kv]
+    # copy the block at the 4 GiB boundary and the last block to the spare one and back
+    for src in (b4, NB - 1):
+        before = from_dev(big_k[src], kv).copy()
+        pa.copy_blocks([big_k], [big_v], [(src, spare)])
+        torch.cuda.synchronize()
+        assert np.array_equal(W.raw_view(from_dev(big_k[spare], kv), kv), W.raw_view(before, kv))
+        assert np.array_equal(W.raw_view(from_dev(big_v[spare], kv), kv),
+                              W.raw_view(from_dev(big_v[src], kv), kv))
+    del big_k, big_v
+    torch.cuda.empty_cache()
+
+
 def test_llama7b_full_size_sampled():
     """64 sequences at context 4096, 17,408-block pool (4 GiB per layer): GPU writes
     and attends over the whole batch; the oracle recomputes sampled sequences from
