@@ -251,13 +251,17 @@ class BlockAllocator:
             fo = self._fo.ctypes.data_as(_c_int32_p)
         _check(lib.pa_alloc_create(num_blocks, block_size, fo, ctypes.byref(self._h)),
                "alloc_create")
+        # kept on the instance: at interpreter exit module globals may be gone
+        # before the last allocator is collected
+        self._destroy = lib.pa_alloc_destroy
         self.num_blocks = num_blocks
         self.block_size = block_size
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            lib.pa_alloc_destroy(h)
+        destroy = getattr(self, "_destroy", None)
+        if h is not None and h.value and destroy is not None:
+            destroy(h)
             self._h = None
 
     def add_seq(self, seq_id: int, num_tokens: int) -> None:

@@ -250,6 +250,91 @@ def test_pools_beyond_4gib(kv, q, H, Hkv):
     torch.cuda.empty_cache()
 
 
+def test_serving_loop_many_steps():
+    """24 decode steps as a server runs them: the library allocator and the
+    oracle's model in lockstep (same tables, slots and copy pairs), prompts
+    written through the cache write, parallel samples forked from partly
+    filled blocks (copy-on-write at their next write), a sequence freed and a
+    new one admitted into reused blocks.  Every step: block copies, cache write
+    and attention on the GPU; the pools match the oracle's bit for bit and the
+    output matches its attention.  Modes cycle through single pass, balanced
+    and partitions."""
+    NB, Hkv, H, D, bs = 96, 2, 8, 64, 8
+    rng = np.random.default_rng(2024)
+    order = rng.permutation(NB).astype(np.int32)
+    lib_alloc = pa.BlockAllocator(NB, bs, order)
+    model = oracle.Allocator(NB, bs, order.tolist())
+    kp = W.empty_pool(NB, Hkv, bs, D, "bf16")
+    vp = W.empty_pool(NB, Hkv, bs, D, "bf16")
+    dk, dv = to_dev(kp, "bf16"), to_dev(vp, "bf16")
+    scale = 1.0 / math.sqrt(D)
+
+    def vals(*shape):
+        return W.to_storage(rng.standard_normal(shape).astype(np.float32), "bf16")
+
+    def write(slots, kn, vn):
+        oracle.kv_write(kp, vp, "bf16", kn, vn, "bf16", slots, bs)
+        pa.kv_cache_write(to_dev(kn, "bf16"), to_dev(vn, "bf16"), dk, dv,
+                          torch.from_numpy(np.asarray(slots, dtype=np.int64)).cuda())
+
+    def admit(sid, prompt):
+        lib_alloc.add_seq(sid, prompt)
+        model.add_seq(sid, prompt)
+        slots = [model.slot(sid, t) for t in range(prompt)]
+        assert slots == [lib_alloc.physical_block(sid, t // bs) * bs + t % bs
+                         for t in range(prompt)]
+        write(slots, vals(prompt, Hkv, D), vals(prompt, Hkv, D))
+
+    def fork(parent, child):
+        lib_alloc.fork(parent, child)
+        model.fork(parent, child)
+
+    def free(sid):
+        lib_alloc.free_seq(sid)
+        model.free_seq(sid)
+
+    live = [0, 1, 2]
+    for sid, prompt in zip(live, (5, 8, 17)):
+        admit(sid, prompt)
+    events = {2: lambda: (fork(0, 10), fork(0, 11), live.extend([10, 11])),
+              10: lambda: (free(1), live.remove(1), admit(3, 12), live.append(3)),
+              16: lambda: (fork(3, 12), live.append(12)),
+              20: lambda: (free(10), live.remove(10))}
+    copies = 0
+    for step in range(24):
+        if step in events:
+            events[step]()
+        slots, pairs = lib_alloc.append_slots(live)
+        m_slots, m_pairs = model.append_slots(live)
+        assert slots.tolist() == list(m_slots)
+        assert [tuple(p) for p in pairs.tolist()] == [tuple(p) for p in m_pairs]
+        copies += len(pairs)
+        if len(pairs):
+            oracle.copy_blocks([kp, vp], [tuple(p) for p in pairs.tolist()])
+            pa.copy_blocks([dk], [dv], pairs)
+        write(slots.tolist(), vals(len(live), Hkv, D), vals(len(live), Hkv, D))
+        max_blocks = 8
+        tables, lens = lib_alloc.export(live, max_blocks)
+        m_tables, m_lens = model.export(live, max_blocks)
+        assert np.array_equal(tables, m_tables) and np.array_equal(lens, m_lens)
+        q = vals(len(live), H, D)
+        ref = oracle.paged_attention(q, "bf16", kp, vp, "bf16", tables, lens, bs, scale)
+        ps = (0, pa.PARTITION_BALANCED, 16)[step % 3]
+        out = torch.full((len(live), H, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+        pa.paged_attention_decode(out, to_dev(q, "bf16"), dk, dv,
+                                  torch.from_numpy(tables).cuda(), torch.from_numpy(lens).cuda(),
+                                  max_context_len=int(lens.max()), scale=scale,
+                                  partition_size=ps)
+        torch.cuda.synchronize()
+        assert np.array_equal(W.raw_view(from_dev(dk, "bf16"), "bf16"), W.raw_view(kp, "bf16"))
+        assert np.array_equal(W.raw_view(from_dev(dv, "bf16"), "bf16"), W.raw_view(vp, "bf16"))
+        err = max_err(out_to_f64(out), ref, "bf16")
+        say(f"    step {step}: live {live} lens {lens.tolist()} pairs {len(pairs)} "
+            f"partition {ps} max-abs error {err:.3g}")
+        assert err <= TOL["bf16"]
+    assert copies >= 3          # the forks from partly filled blocks were copied on write
+
+
 def test_llama7b_full_size_sampled():
     """64 sequences at context 4096, 17,408-block pool (4 GiB per layer): GPU writes
     and attends over the whole batch; the oracle recomputes sampled sequences from
