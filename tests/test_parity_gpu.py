@@ -335,6 +335,68 @@ def test_serving_loop_many_steps():
     assert copies >= 3          # the forks from partly filled blocks were copied on write
 
 
+def test_two_threads_two_streams():
+    """Two host threads, each with its own stream and workspace, run cache
+    writes and attention on different cases at the same time (the library
+    keeps no device state between calls; its host caches are locked).  Both
+    match the oracle in every mode."""
+    import threading
+    cases = [W.make_decode_case("threads_gqa", "tiny", num_seqs=40, num_heads=16, num_kv_heads=2,
+                                head_dim=128, block_size=16,
+                                context_lens=np.random.default_rng(1).integers(1, 900, 40).tolist(),
+                                kv_dtype="bf16", q_dtype="bf16", spare_blocks=5, salt=1),
+             W.make_decode_case("threads_mha", "tiny", num_seqs=24, num_heads=8, num_kv_heads=8,
+                                head_dim=64, block_size=32,
+                                context_lens=np.random.default_rng(2).integers(0, 1500, 24).tolist(),
+                                kv_dtype="fp8_e4m3", q_dtype="f16", spare_blocks=5, salt=2)]
+    refs = [oracle_step(c) for c in cases]
+    devs = [DeviceCase(c) for c in cases]
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(i):
+        try:
+            c, d = cases[i], devs[i]
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                pa.kv_cache_write(d.k_new, d.v_new, d.k_pool, d.v_pool, d.slots,
+                                  k_scale=c.k_scale, v_scale=c.v_scale, stream=st)
+                for rep in range(4):
+                    for ps in (0, pa.PARTITION_BALANCED, 256):
+                        need = pa.paged_attention_workspace_size(
+                            c.num_seqs, c.num_heads, c.num_kv_heads, c.head_dim,
+                            c.max_context_len, ps)
+                        ws = pa.new_workspace(need, "cuda")
+                        out = torch.full_like(d.q, float("nan"))
+                        pa.paged_attention_decode(out, d.q, d.k_pool, d.v_pool, d.tables, d.ctx,
+                                                  max_context_len=c.max_context_len,
+                                                  scale=c.scale, k_scale=c.k_scale,
+                                                  v_scale=c.v_scale, partition_size=ps,
+                                                  workspace=ws, stream=st)
+                        results[(i, rep, ps)] = out
+            st.synchronize()
+        except Exception as e:              # reported by the main thread
+            errors.append(repr(e))
+
+    say("[case] two threads, two streams")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i, (c, d) in enumerate(zip(cases, devs)):
+        kp, vp, ref = refs[i]
+        assert_pools_equal(d, kp, vp)
+        for (j, rep, ps), out in results.items():
+            if j == i:
+                err = max_err(out_to_f64(out), ref, c.q_dtype)
+                assert err <= TOL[c.kv_dtype], (c.name, rep, ps, err)
+    say(f"    {len(results)} launches checked")
+
+
 def test_llama7b_full_size_sampled():
     """64 sequences at context 4096, 17,408-block pool (4 GiB per layer): GPU writes
     and attends over the whole batch; the oracle recomputes sampled sequences from
