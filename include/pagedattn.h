@@ -16,6 +16,11 @@
  * functions return once the work is enqueued.  Argument errors are detected
  * on the host before anything is enqueued and leave every buffer untouched.
  * Faults inside kernels surface at the caller's next synchronisation.
+ * The device entry points keep no device state between calls and may be
+ * called from several host threads at once, on the same or different
+ * streams. Calls that write the same buffers (pools, outputs or a
+ * workspace) must be ordered by the caller. The host allocator below is
+ * the exception: serialise the calls on each of its handles.
  *
  * KV pool layout (one pool for K and one for V, per layer), dense row-major:
  *     pool[num_blocks][num_kv_heads][block_size][head_dim]
