@@ -83,7 +83,7 @@ class Workload:
     def step(self):
         if self.pairs is not None and len(self.pairs):
             self.pa.copy_blocks([d["k_pool"] for d in self.layers],
-                                [d["v_pool"] for d in self.layers], self.pairs)
+                                [d["v_pool"] for d in self.layers], self.pairs_d)
         for l in range(self.L):
             d = self.layers[l]
             self.pa.kv_cache_write(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], self.slots,
@@ -96,40 +96,72 @@ class Workload:
                 "block_size": self.bs, "kv_dtype": self.kv_dtype, "q_dtype": self.q_dtype,
                 "context_lens": self.ctx_desc, "partition_size": self.partition_size}
 
-    def cpu_sample(self, oracle, budget_s):
-        """Oracle write + attention, one sequence (all heads) of layer 0 at a time."""
+    def cpu_inputs(self, l, s):
+        """Host copies of what the oracle needs for sequence s of layer l: the
+        sequence's blocks (a local table 0..n-1), its new K/V and its query."""
         torch = self.torch
-        d = self.layers[0]
-        tables = self.tables.cpu().numpy()
-        ctx = self.ctx
-        done, secs, bytes_done = 0, 0.0, 0
-        kn_all, vn_all = d["k_new"].cpu(), d["v_new"].cpu()
-        q_all = d["q"].cpu()
-        slots = self.slots.cpu().numpy()
-        order = np.argsort(-ctx, kind="stable")          # longest first: the work that matters
-        for s in order:
-            if secs >= budget_s:
-                break
-            n = int(ctx[s])
-            nblk = (n + self.bs - 1) // self.bs
-            idx = torch.from_numpy(tables[s, :nblk].astype(np.int64)).cuda()
-            kp, vp = raw_np(d["k_pool"][idx]), raw_np(d["v_pool"][idx])
-            local = np.arange(nblk, dtype=np.int32)[None, :]
-            pos = n - 1
-            slot = np.array([(pos // self.bs) * self.bs + pos % self.bs])
-            kn, vn = raw_np(kn_all[s:s + 1]), raw_np(vn_all[s:s + 1])
-            q = raw_np(q_all[s:s + 1])
-            t0 = time.perf_counter()
-            oracle.kv_write(kp, vp, self.kv_dtype, kn, vn, self.q_dtype, slot, self.bs,
-                            self.k_scale, self.v_scale)
-            oracle.paged_attention(q, self.q_dtype, kp, vp, self.kv_dtype, local, [n], self.bs,
-                                   self.scale, self.k_scale, self.v_scale)
-            secs += time.perf_counter() - t0
-            done += 1
-            bytes_done += n * 2 * self.Hkv * self.D * ELEM[self.kv_dtype]
-        sample = (f"{done} sequence-layers of layer 0 (one sequence, all {self.H} heads, "
-                  f"longest contexts first, {bytes_done / 1e6:.1f} MB of K/V)")
-        return done, secs, bytes_done, sample
+        d = self.layers[l]
+        n = int(self.ctx[s])
+        nblk = (n + self.bs - 1) // self.bs
+        if not hasattr(self, "_tables_np"):
+            self._tables_np = self.tables.cpu().numpy()
+        idx = torch.from_numpy(self._tables_np[s, :nblk].astype(np.int64)).cuda()
+        kp, vp = raw_np(d["k_pool"][idx]), raw_np(d["v_pool"][idx])
+        pos = n - 1
+        slot = np.array([(pos // self.bs) * self.bs + pos % self.bs])
+        return dict(kp=kp, vp=vp, kn=raw_np(d["k_new"][s:s + 1]), vn=raw_np(d["v_new"][s:s + 1]),
+                    q=raw_np(d["q"][s:s + 1]), slot=slot, n=n,
+                    local=np.arange(nblk, dtype=np.int32)[None, :])
+
+    def cpu_run(self, oracle, x):
+        """The oracle as it stands: cache write, then attention, for one sequence-layer."""
+        oracle.kv_write(x["kp"], x["vp"], self.kv_dtype, x["kn"], x["vn"], self.q_dtype, x["slot"],
+                        self.bs, self.k_scale, self.v_scale)
+        oracle.paged_attention(x["q"], self.q_dtype, x["kp"], x["vp"], self.kv_dtype, x["local"],
+                               [x["n"]], self.bs, self.scale, self.k_scale, self.v_scale)
+
+    def cpu_sample(self, oracle, budget_s, cores):
+        """Oracle throughput on a bounded sample: sequence-layers, longest contexts
+        first, layer after layer, run `cores` at a time on a thread pool (NumPy
+        releases the interpreter lock in its array loops).  Only the oracle calls
+        are timed; copying each batch's inputs to the host is not."""
+        import concurrent.futures as cf
+        order = np.argsort(-self.ctx, kind="stable")
+        work = [(l, int(s)) for l in range(self.L) for s in order]
+        done, secs, kv_bytes, i = 0, 0.0, 0, 0
+        with cf.ThreadPoolExecutor(cores) as ex:
+            while i < len(work) and secs < budget_s:
+                batch = work[i:i + cores]
+                i += len(batch)
+                xs = [self.cpu_inputs(l, s) for l, s in batch]
+                t0 = time.perf_counter()
+                list(ex.map(lambda x: self.cpu_run(oracle, x), xs))
+                secs += time.perf_counter() - t0
+                done += len(batch)
+                kv_bytes += sum(x["n"] for x in xs) * 2 * self.Hkv * self.D * ELEM[self.kv_dtype]
+        layers = len({l for l, _ in work[:i]})
+        sample = (f"{done} sequence-layers (all {self.H} heads each) from {layers} layer(s), longest "
+                  f"contexts first, {kv_bytes / 1e6:.1f} MB of K/V, {cores} at a time")
+        return {"value": round(done / secs, 3), "unit": "seq-layers/s", "cores": cores,
+                "kind": "oracle", "sample": sample, "cpu_model": cpu_model(),
+                "host_cpus": os.cpu_count(), "seconds": round(secs, 2),
+                "kv_gbs_equivalent": round(kv_bytes / secs / 1e9, 3)}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_cores():
+    """Threads for the oracle baseline: every core this process may run on, at
+    most 16 (one GPU's share of the host)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
@@ -261,6 +293,7 @@ class Llama70B(HostLayers):
         case, pairs = W.shared_prompt_case(alloc, spec, num_blocks=NB)
         self.place(torch, case, args.layers or 8)
         self.pairs = pairs
+        self.pairs_d = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32)).cuda()
         P, n_ind = spec.prompt_len, len(spec.independent_ctx)
         # shared full prompt blocks are read once; every sample owns its copied last block
         full = (P // 16) * 16
@@ -360,6 +393,88 @@ def reference_copy_gbs(torch, mib=512, reps=10):
     return gbs
 
 
+def measure(wl, torch, steps, warmup, decode_iters, graph=True, singles=True):
+    """Time `steps` whole steps (after `warmup`), then the decode call alone back
+    to back over the layers, then (optionally) single calls between their own
+    events.  Graphs are replayed unless `graph` is false."""
+    step_fn = wl.step
+    decode_fn = lambda: [wl.decode(l) for l in range(wl.L)]
+    for _ in range(max(1, warmup)):
+        step_fn()
+    torch.cuda.synchronize()
+    graphs = []
+    if graph:
+        g_step, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_step):
+            wl.step()
+        with torch.cuda.graph(g_dec):
+            decode_fn()
+        graphs = [g_step, g_dec]
+        step_fn, decode_fn = g_step.replay, g_dec.replay
+        for _ in range(max(1, warmup)):
+            step_fn()
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step_fn()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / steps
+    rounds = max(1, decode_iters // wl.L)
+    start.record()
+    for _ in range(rounds):
+        decode_fn()
+    end.record()
+    torch.cuda.synchronize()
+    decode_ms = start.elapsed_time(end) / (rounds * wl.L)
+    spread = None
+    if singles:
+        times = []
+        for i in range(max(10, min(60, decode_iters))):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            wl.decode(i % wl.L)
+            b.record()
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e3)
+        spread = [round(float(np.percentile(times, q)), 2) for q in (10, 50, 90)]
+    del graphs
+    return ms_per_step, decode_ms, spread
+
+
+def config_entry(key, wl, torch, oracle, args, cpu_seconds, cores):
+    """Measurements of one workload for the per-config list of the bench line."""
+    ms, dec_ms, spread = measure(wl, torch, args.steps, args.warmup, args.decode_iters,
+                                 graph=not args.no_graph)
+    achieved = wl.attn_bytes / (dec_ms * 1e-3) / 1e9
+    traffic, src = read_traffic(key, wl.partition_size, wl.bs)
+    e = {"workload": key, "config": wl.config(), "ms_per_step": round(ms, 4),
+         "step_gbs": round(wl.step_bytes / (ms * 1e-3) / 1e9, 1),
+         "decode_tokens_per_s": round(wl.seq_layers_per_step / (ms * 1e-3), 1),
+         "attention": {"avg_launch_us": round(dec_ms * 1e3, 2), "achieved_gbs": round(achieved, 1),
+                       "frac": round(achieved / PEAK_HBM_GBS, 4),
+                       "algorithmic_bytes_per_launch": wl.attn_bytes,
+                       "single_call_us_p10_p50_p90": spread, "traffic": traffic,
+                       "traffic_ratio": None if traffic is None else round(traffic / wl.attn_bytes, 4),
+                       "traffic_source": src}}
+    if hasattr(wl, "logical_attn_bytes"):
+        e["attention"]["logical_bytes_per_launch"] = wl.logical_attn_bytes
+    log(f"[{key} bs{wl.bs}] {ms:.3f} ms/step, attention {dec_ms * 1e3:.1f} us "
+        f"({achieved:.0f} GB/s, {achieved / PEAK_HBM_GBS:.3f} of peak)")
+    if cpu_seconds > 0:
+        e["cpu_baseline"] = wl.cpu_sample(oracle, cpu_seconds, cores)
+        log(f"[{key}] cpu oracle: {e['cpu_baseline']['value']} seq-layers/s on {cores} threads")
+    return e
+
+
+# every configuration of the workload set, measured after the headline one
+CONFIG_SET = [("tiny", {}), ("opt13b", {}), ("llama70b", {}), ("falcon7b", {"block_size": 8}),
+              ("falcon7b", {"block_size": 16}), ("falcon7b", {"block_size": 32}),
+              ("falcon7b", {"block_size": 64})]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -369,8 +484,12 @@ def main():
     ap.add_argument("--partition-size", type=int, default=None,
                     help="0 single pass, > 0 split-context partitions, -1 balanced split "
                          "(default: the fastest measured for the workload)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="budget of the CPU-oracle baseline sample (0 = skip)")
+    ap.add_argument("--config-cpu-seconds", type=float, default=3.0,
+                    help="CPU-oracle budget for each entry of the per-config list")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="measure the chosen workload only (no per-config list)")
     ap.add_argument("--decode-iters", type=int, default=64)
     ap.add_argument("--block-size", type=int, default=0, help="falcon7b: block size (default 16)")
     ap.add_argument("--layers", type=int, default=0, help="llama70b: layers per step (default 8)")
@@ -400,56 +519,12 @@ def main():
     if args.partition_size is None:
         args.partition_size = DEFAULT_PARTITION[args.workload]
     wl = WORKLOADS[args.workload](pa, W, torch, args.partition_size, args)
-
-    # one step and one round of decode launches (every layer once), eager or as HIP graphs
-    step_fn = wl.step
-    decode_fn = lambda: [wl.decode(l) for l in range(wl.L)]
-    for _ in range(max(1, args.warmup)):
-        step_fn()
-    torch.cuda.synchronize()
-    if not args.no_graph:
-        g_step, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_step):
-            wl.step()
-        with torch.cuda.graph(g_dec):
-            decode_fn()
-        step_fn, decode_fn = g_step.replay, g_dec.replay
-        for _ in range(max(1, args.warmup)):
-            step_fn()
-        torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps, graph={not args.no_graph})")
-
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step_fn()
-    end.record()
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
+    ms_per_step, decode_ms, spread = measure(wl, torch, args.steps, args.warmup,
+                                             args.decode_iters, graph=not args.no_graph)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
-
-    # dominant kernel: decode attention alone, back to back over the layers
-    rounds = max(1, args.decode_iters // wl.L)
-    start.record()
-    for _ in range(rounds):
-        decode_fn()
-    end.record()
-    torch.cuda.synchronize()
-    decode_ms = start.elapsed_time(end) / (rounds * wl.L)
     achieved = wl.attn_bytes / (decode_ms * 1e-3) / 1e9
     log(f"decode attention: {decode_ms * 1e3:.1f} us per launch, {achieved:.0f} GB/s")
-    # spread of single calls (eager, each between its own events on the launch stream)
-    singles = []
-    for i in range(max(10, min(60, args.decode_iters))):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        wl.decode(i % wl.L)
-        b.record()
-        b.synchronize()
-        singles.append(a.elapsed_time(b) * 1e3)
-    p10, p50, p90 = (float(np.percentile(singles, q)) for q in (10, 50, 90))
-    log(f"single calls: p10 {p10:.1f} p50 {p50:.1f} p90 {p90:.1f} us")
+    log(f"single calls: p10 {spread[0]} p50 {spread[1]} p90 {spread[2]} us")
 
     value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
     traffic, traffic_src = read_traffic(args.workload, args.partition_size, wl.bs)
@@ -473,20 +548,31 @@ def main():
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "paged_attention_decode",
                      "avg_launch_us": round(decode_ms * 1e3, 2),
-                     "single_call_us_p10_p50_p90": [round(p10, 2), round(p50, 2), round(p90, 2)],
+                     "single_call_us_p10_p50_p90": spread,
                      "algorithmic_bytes_per_launch": wl.attn_bytes,
                      "traffic_source": traffic_src,
                      "reference_copy_gbs": round(copy_gbs, 1)},
         "cpu_baseline": None,
     }
-
+    import oracle
+    cores = cpu_cores()
     if args.cpu_seconds > 0:
-        import oracle
-        done, secs, kv_bytes, sample = wl.cpu_sample(oracle, args.cpu_seconds)
-        line["cpu_baseline"] = {"value": round(done / secs, 3), "unit": "seq-layers/s",
-                                "cores": 1, "kind": "oracle", "sample": sample,
-                                "kv_gbs_equivalent": round(kv_bytes / secs / 1e9, 3)}
-        log(f"cpu oracle: {done} seq-layers in {secs:.1f}s")
+        line["cpu_baseline"] = wl.cpu_sample(oracle, args.cpu_seconds, cores)
+        log(f"cpu oracle: {line['cpu_baseline']['value']} seq-layers/s on {cores} threads")
+
+    if not args.no_configs:
+        del wl
+        torch.cuda.empty_cache()
+        entries = []
+        for key, over in CONFIG_SET:
+            a = argparse.Namespace(**vars(args))
+            a.block_size = over.get("block_size", 0)
+            ps = DEFAULT_PARTITION[key]
+            w = WORKLOADS[key](pa, W, torch, ps, a)
+            entries.append(config_entry(key, w, torch, oracle, args, args.config_cpu_seconds, cores))
+            del w
+            torch.cuda.empty_cache()
+        line["configs"] = entries
     print(json.dumps(line), flush=True)
 
 

@@ -179,11 +179,22 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
  * block is copied and the write goes into the copy (KV 缓存与分页注意力
  * §08 共用，写时复制).  Issue it on the same stream before the cache write.
  *
- *   k_pools, v_pools  HOST arrays of num_layers DEVICE pool pointers
- *   pairs             HOST int32 [num_pairs][2] = (src, dst), e.g. as
- *                     returned by pa_alloc_append_slots.  Every id must lie
- *                     in [0, num_blocks), destinations must be distinct, and
- *                     no destination may also be a source in the same call.
+ *   k_pools, v_pools  HOST arrays of num_layers DEVICE pool pointers (their
+ *                     values are baked into the launches: a captured graph
+ *                     keeps copying the same pools)
+ *   pairs             DEVICE int32 [num_pairs][2] = (src, dst), 8-byte
+ *                     aligned, e.g. the pairs pa_alloc_append_slots returned,
+ *                     copied to the device.  The pairs are read by the kernel
+ *                     when it runs, so one captured launch can be replayed
+ *                     with new pairs written into the same buffer each step.
+ *                     A pair with an id outside [0, num_blocks) — such as
+ *                     -1 padding of a fixed-capacity buffer — or with
+ *                     src == dst is skipped.  Destinations must be distinct
+ *                     and no destination may also be a source in the same
+ *                     call (the caller's contract, not checked: the copies
+ *                     run concurrently, so a violation gives undefined bytes
+ *                     in the blocks concerned).
+ *   num_pairs         rows of `pairs` the launch covers (its capacity).
  *   num_pairs == 0 or num_layers == 0 is a no-op.
  */
 pa_status pa_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,

@@ -47,7 +47,7 @@ _SIGNATURES = [
       ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
     ("pa_copy_blocks", ctypes.c_int32,
      [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _c_int32_p, ctypes.c_int32, _vp]),
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
     ("pa_alloc_create", ctypes.c_int32,
      [ctypes.c_int32, ctypes.c_int32, _c_int32_p, ctypes.POINTER(_vp)]),
     ("pa_alloc_destroy", None, [_vp]),
@@ -208,7 +208,10 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, *
                 *([workspace] if workspace is not None else []))
     need = paged_attention_workspace_size(S, H, Hkv, D, max_context_len, partition_size)
     if need and workspace is None:
-        workspace = new_workspace(need, q.device)
+        # allocated in the order of the stream the kernels run on, so that the
+        # caching allocator reuses it only after they are done
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(q.device)):
+            workspace = new_workspace(need, q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib.pa_paged_attention_decode(
@@ -220,23 +223,47 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, *
 
 
 def copy_blocks(k_pools: Sequence, v_pools: Sequence, pairs, *, stream=None) -> None:
-    """Copy block src -> dst for every (src, dst) in ``pairs`` in every layer's K and V pool."""
-    pairs = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    """Copy block src -> dst for every (src, dst) in ``pairs`` in every layer's K and V pool.
+
+    ``pairs`` is a device int32 tensor [N, 2] (read by the kernel when it
+    runs: a captured launch replays with whatever the buffer holds; rows with
+    an id outside the pool, e.g. -1 padding, are skipped), or host pairs
+    (a sequence or array), which are copied to the device on the call's stream
+    first."""
+    torch = _torch()
     L = len(k_pools)
     if L != len(v_pools):
         raise ValueError("k_pools and v_pools differ in length")
-    if L == 0 or len(pairs) == 0:
+    if L == 0:
         return
     NB, Hkv, bs, D = k_pools[0].shape
     for p in list(k_pools) + list(v_pools):
         if p.shape != k_pools[0].shape or p.dtype != k_pools[0].dtype:
             raise ValueError("all pools must share shape and dtype")
     _one_device(*k_pools, *v_pools)
+    dev = k_pools[0].device
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    if isinstance(pairs, torch.Tensor) and pairs.is_cuda:
+        if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+            raise ValueError("device pairs must be int32 [N, 2]")
+        _one_device(k_pools[0], pairs)
+        dpairs = pairs
+    else:
+        host = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+        if len(host) == 0:
+            return
+        if torch.cuda.is_current_stream_capturing():
+            raise ValueError("copy_blocks under graph capture needs device pairs (a host "
+                             "array would be read at capture time only)")
+        with torch.cuda.stream(s):          # allocated and filled in the call's stream order
+            dpairs = torch.from_numpy(host).to(dev)
+    if dpairs.shape[0] == 0:
+        return
     kp = (ctypes.c_void_p * L)(*[_dev(p, "k_pool").value for p in k_pools])
     vp = (ctypes.c_void_p * L)(*[_dev(p, "v_pool").value for p in v_pools])
     _check(lib.pa_copy_blocks(kp, vp, L, dtype_code(k_pools[0]), Hkv, D, bs, NB,
-                              pairs.ctypes.data_as(_c_int32_p), len(pairs),
-                              _stream(stream, k_pools[0].device)), "copy_blocks")
+                              _dev(dpairs, "pairs"), dpairs.shape[0],
+                              ctypes.c_void_p(s.cuda_stream)), "copy_blocks")
 
 
 # ------------------------------------------------------------------ host allocator

@@ -6,7 +6,6 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
-#include <unordered_set>
 
 #include "kernels.h"
 #include "pa_device.h"
@@ -243,38 +242,28 @@ pa_status pa_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num
         (int64_t)num_kv_heads * block_size * head_dim * pa::elem_bytes(kv_dtype);
     if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
     if (num_layers == 0 || num_pairs == 0) return PA_OK;
-    if (!k_pools || !v_pools || !pairs) return PA_ERR_INVALID_ARG;
+    if (!k_pools || !v_pools || !pairs || (reinterpret_cast<uintptr_t>(pairs) & 7u))
+        return PA_ERR_INVALID_ARG;
     for (int32_t l = 0; l < num_layers; ++l)
         if (!k_pools[l] || !v_pools[l] || !aligned16(k_pools[l]) || !aligned16(v_pools[l]))
             return PA_ERR_INVALID_ARG;
-    std::unordered_set<int32_t> dsts, srcs;
-    for (int32_t i = 0; i < num_pairs; ++i) {
-        const int32_t s = pairs[2 * i], d = pairs[2 * i + 1];
-        if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks || s == d) return PA_ERR_INVALID_ARG;
-        if (!dsts.insert(d).second) return PA_ERR_INVALID_ARG;
-        srcs.insert(s);
-    }
-    for (int32_t d : dsts)
-        if (srcs.count(d)) return PA_ERR_INVALID_ARG;
+    const int64_t slices = (block_bytes + 4095) / 4096;
+    if ((int64_t)num_pairs * slices > INT32_MAX) return PA_ERR_UNSUPPORTED;
 
     for (int32_t l0 = 0; l0 < num_layers; l0 += pa::kCopyMaxLayers) {
-        for (int32_t p0 = 0; p0 < num_pairs; p0 += pa::kCopyMaxPairs) {
-            pa::CopyArgs a{};
-            a.block_bytes = block_bytes;
-            a.num_layers = std::min(num_layers - l0, pa::kCopyMaxLayers);
-            a.num_pairs = std::min(num_pairs - p0, pa::kCopyMaxPairs);
-            for (int32_t l = 0; l < a.num_layers; ++l) {
-                a.k[l] = k_pools[l0 + l];
-                a.v[l] = v_pools[l0 + l];
-            }
-            for (int32_t i = 0; i < a.num_pairs; ++i) {
-                a.src[i] = pairs[2 * (p0 + i)];
-                a.dst[i] = pairs[2 * (p0 + i) + 1];
-            }
-            const pa_status st =
-                launch_checked([&] { return pa::launch_copy_blocks(a, as_stream(stream)); });
-            if (st != PA_OK) return st;
+        pa::CopyArgs a{};
+        a.pairs = pairs;
+        a.block_bytes = block_bytes;
+        a.num_blocks = num_blocks;
+        a.num_pairs = num_pairs;
+        a.num_layers = std::min(num_layers - l0, pa::kCopyMaxLayers);
+        for (int32_t l = 0; l < a.num_layers; ++l) {
+            a.k[l] = k_pools[l0 + l];
+            a.v[l] = v_pools[l0 + l];
         }
+        const pa_status st =
+            launch_checked([&] { return pa::launch_copy_blocks(a, as_stream(stream)); });
+        if (st != PA_OK) return st;
     }
     return PA_OK;
 }

@@ -23,18 +23,18 @@ struct WriteArgs {
 };
 hipError_t launch_kv_write(const WriteArgs& a, int src_dt, int kv_dt, hipStream_t stream);
 
-constexpr int kCopyMaxLayers = 32;
-constexpr int kCopyMaxPairs = 64;
+constexpr int kCopyMaxLayers = 32;        // layers per copy launch (pointers in the arguments)
 struct CopyArgs {
     void* k[kCopyMaxLayers];
     void* v[kCopyMaxLayers];
-    int32_t src[kCopyMaxPairs];
-    int32_t dst[kCopyMaxPairs];
+    const int32_t* pairs;       // DEVICE int32 [num_pairs][2] = (src, dst)
     int64_t block_bytes;        // one block of one pool, a multiple of 16
+    int32_t num_blocks;         // pairs with an id outside [0, num_blocks) are skipped
     int32_t num_layers;         // <= kCopyMaxLayers
-    int32_t num_pairs;          // <= kCopyMaxPairs
+    int32_t num_pairs;
+    int32_t slices;             // 4 KiB slices per block (set at launch)
 };
-hipError_t launch_copy_blocks(const CopyArgs& a, hipStream_t stream);
+hipError_t launch_copy_blocks(CopyArgs& a, hipStream_t stream);
 
 // Sequences are scheduled in windows of kWindow (their metadata is staged in
 // LDS).  The balanced schedule gives each worker (a wavefront) two

@@ -141,24 +141,30 @@ def test_write_zero_tokens_is_noop():
     assert write_call(T=0, k_new=NULL) == 0
 
 
-def copy_call(pairs, **kw):
+def copy_call(**kw):
+    """pa_copy_blocks with fake device addresses: only calls that the host-side
+    checks reject (or that are no-ops) are made, so nothing is launched."""
     kp = (ctypes.c_void_p * 2)(0x1000, 0x2000)
     vp = (ctypes.c_void_p * 2)(0x3000, 0x4000)
-    arr = (ctypes.c_int32 * (2 * max(1, len(pairs))))(*[x for p in pairs for x in p])
-    args = dict(k=kp, v=vp, L=2, dt=1, Hkv=2, D=64, bs=16, NB=8, pairs=arr, n=len(pairs), stream=NULL)
+    args = dict(k=kp, v=vp, L=2, dt=1, Hkv=2, D=64, bs=16, NB=8, pairs=ctypes.c_void_p(0x5000),
+                n=1, stream=NULL)
     args.update(kw)
     return lib.pa_copy_blocks(*args.values())
 
 
-@pytest.mark.parametrize("pairs", [[(0, 8)], [(-1, 2)], [(1, 1)], [(1, 2), (3, 2)], [(1, 2), (2, 3)]])
-def test_copy_validation(pairs):
-    assert copy_call(pairs) == -1
+@pytest.mark.parametrize("kw", [dict(pairs=NULL), dict(pairs=ctypes.c_void_p(0x5004)), dict(n=-1),
+                                dict(NB=0), dict(bs=12), dict(L=-1), dict(dt=7)])
+def test_copy_validation(kw):
+    assert copy_call(**kw) == -1
 
 
 def test_copy_noop_and_null_pool():
-    assert copy_call([], n=0) == 0
+    assert copy_call(n=0) == 0
+    assert copy_call(L=0) == 0
     kp = (ctypes.c_void_p * 2)(0x1000, 0)
-    assert copy_call([(1, 2)], k=kp) == -1
+    assert copy_call(k=kp) == -1
+    kp = (ctypes.c_void_p * 2)(0x1000, 0x2008)          # pool not 16-byte aligned
+    assert copy_call(k=kp) == -1
 
 
 # ------------------------------------------------------------------ binding checks (host only)

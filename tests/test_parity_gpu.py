@@ -147,10 +147,11 @@ def test_whole_step_graph_replays(kind, ps):
                                              case.head_dim, case.max_context_len, ps)
     ws = pa.new_workspace(need, "cuda")
     out = torch.full_like(dev.q, float("nan"))
+    dpairs = torch.from_numpy(np.ascontiguousarray(pairs, dtype=np.int32).reshape(-1, 2)).cuda()
 
     def step():
         if len(pairs):
-            pa.copy_blocks([dev.k_pool], [dev.v_pool], pairs)
+            pa.copy_blocks([dev.k_pool], [dev.v_pool], dpairs)
         dev.write()
         pa.paged_attention_decode(out, dev.q, dev.k_pool, dev.v_pool, dev.tables, dev.ctx,
                                   max_context_len=case.max_context_len, scale=case.scale,
@@ -617,6 +618,56 @@ def test_copy_blocks_bit_exact_many_layers_and_pairs(dt):
     oracle.copy_blocks(pools_np, [tuple(p) for p in pairs])
     for g, r in zip(dev, pools_np):
         assert np.array_equal(W.raw_view(from_dev(g, dt), dt), W.raw_view(r, dt))
+
+
+def test_copy_blocks_device_pairs_skip_padding():
+    """Pairs read from device memory: rows with an id outside the pool (-1
+    padding, >= num_blocks) or with src == dst are skipped; the rest are
+    copied bit for bit."""
+    L, NB, Hkv, bs, D, dt = 3, 64, 2, 16, 64, "bf16"
+    rng = np.random.default_rng(11)
+    pools_np = [rng.integers(0, 65535, size=(NB, Hkv, bs, D), dtype=np.uint16) for _ in range(2 * L)]
+    pairs = np.array([[3, 9], [-1, -1], [5, 70], [4, 4], [12, 1], [-1, 20], [63, 0]], np.int32)
+    dev = [to_dev(p, dt) for p in pools_np]
+    say(f"[case] copy_blocks device pairs with padding rows={len(pairs)}")
+    pa.copy_blocks(dev[:L], dev[L:], torch.from_numpy(pairs).cuda())
+    torch.cuda.synchronize()
+    oracle.copy_blocks(pools_np, [(3, 9), (12, 1), (63, 0)])
+    for g, r in zip(dev, pools_np):
+        assert np.array_equal(from_dev(g, dt), r)
+
+
+def test_copy_blocks_graph_replays_new_pairs():
+    """One captured copy_blocks launch over a fixed-capacity device pair buffer,
+    replayed with two different pair sets written into the buffer between
+    replays (the copy-on-write pairs of two different steps): each replay is
+    bit-exact against the oracle's block copy of that step's pairs."""
+    L, NB, Hkv, bs, D, dt, cap = 4, 96, 2, 16, 128, "f16", 16
+    rng = np.random.default_rng(12)
+    base = [rng.integers(0, 65535, size=(NB, Hkv, bs, D), dtype=np.uint16).view(np.float16)
+            for _ in range(2 * L)]
+    dev = [to_dev(p, dt) for p in base]
+    buf = torch.full((cap, 2), -1, dtype=torch.int32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        pa.copy_blocks(dev[:L], dev[L:], buf)
+    perm = rng.permutation(NB)
+    steps = [np.stack([perm[:5], perm[5:10]], axis=1), np.stack([perm[20:31], perm[40:51]], axis=1)]
+    for i, pairs in enumerate(steps):
+        host = np.full((cap, 2), -1, np.int32)
+        host[:len(pairs)] = pairs
+        buf.copy_(torch.from_numpy(host))
+        for d, b in zip(dev, base):
+            d.copy_(torch.from_numpy(b))
+        torch.cuda.synchronize()
+        say(f"[case] copy_blocks graph replay {i} pairs={len(pairs)}")
+        g.replay()
+        torch.cuda.synchronize()
+        ref = [b.copy() for b in base]
+        oracle.copy_blocks(ref, [tuple(p) for p in pairs.tolist()])
+        for d, r in zip(dev, ref):
+            assert np.array_equal(from_dev(d, dt).view(np.uint16), r.view(np.uint16)), i
 
 
 # ------------------------------------------------------------------ grouped heads (matrix-core path)
