@@ -172,6 +172,40 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
                                     int32_t partition_size, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/* Size of the device scratch the allocation-free decode entry point uses
+ * (one copy per GPU, held from the library's load until the process ends). */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * paged_attention_decode_noalloc — pa_paged_attention_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments, meaning and
+ * result as pa_paged_attention_decode without the workspace: the split modes'
+ * partial records and range descriptors go to a static device array of
+ * PA_NOALLOC_SCRATCH_BYTES inside the library instead.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine); the scratch needs no
+ * initial contents, and every call writes what it later reads.
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (different streams, or host threads without ordering) race and
+ * give undefined outputs; order them.  A launch whose records exceed the
+ * scratch returns PA_ERR_WORKSPACE with nothing enqueued (the balanced split
+ * needs (head_dim + 2) * 4 bytes per record, two records per worker and head
+ * of its unit; e.g. about 8.5 MB for 128 sequences of 64 query heads over 8
+ * KV heads of 128); partition_size > 0 needs what
+ * pa_paged_attention_workspace_size returns.  PA_ERR_HIP if the runtime
+ * cannot give the scratch's address.
+ */
+pa_status pa_paged_attention_decode_noalloc(void* out, const void* q, int32_t q_dtype,
+                                            const void* k_pool, const void* v_pool,
+                                            int32_t kv_dtype, const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq,
+                                            const int32_t* context_lens, int32_t max_context_len,
+                                            int32_t num_seqs, int32_t num_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t block_size, int32_t num_blocks, float scale,
+                                            float k_scale, float v_scale, int32_t partition_size,
+                                            void* stream);
+
 /*
  * copy_blocks — the data half of copy-on-write: for each pair (src, dst),
  * copy physical block src to dst, bit for bit, in the K and V pool of every

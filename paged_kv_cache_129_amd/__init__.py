@@ -45,6 +45,11 @@ _SIGNATURES = [
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
       ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
+    ("pa_paged_attention_decode_noalloc", ctypes.c_int32,
+     [_vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+      ctypes.c_int32, _vp]),
     ("pa_copy_blocks", ctypes.c_int32,
      [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
@@ -220,6 +225,35 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, *
         block_tables.shape[1], _dev(context_lens, "context_lens"), int(max_context_len), S, H,
         Hkv, D, bs, NB, float(scale), float(k_scale), float(v_scale), int(partition_size),
         ws_ptr, ws_bytes, _stream(stream, q.device)), "paged_attention_decode")
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def paged_attention_decode_noalloc(out, q, k_pool, v_pool, block_tables, context_lens, *,
+                                   max_context_len: int, scale: float, k_scale: float = 1.0,
+                                   v_scale: float = 1.0, partition_size: int = 0,
+                                   stream=None) -> None:
+    """paged_attention_decode without a workspace: the split modes use the
+    library's static per-GPU scratch (nothing is allocated; calls that overlap
+    on one GPU race)."""
+    torch = _torch()
+    S, H, D = q.shape
+    NB, Hkv, bs, D2 = k_pool.shape
+    if D2 != D or out.shape != q.shape or out.dtype != q.dtype or v_pool.shape != k_pool.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [S, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
+        raise ValueError("context_lens must be int32 [S]")
+    _same_dtype(k_pool, v_pool, "k_pool", "v_pool")
+    _one_device(out, q, k_pool, v_pool, block_tables, context_lens)
+    _check(lib.pa_paged_attention_decode_noalloc(
+        _dev(out, "out"), _dev(q, "q"), dtype_code(q), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"), dtype_code(k_pool), _dev(block_tables, "block_tables"),
+        block_tables.shape[1], _dev(context_lens, "context_lens"), int(max_context_len), S, H,
+        Hkv, D, bs, NB, float(scale), float(k_scale), float(v_scale), int(partition_size),
+        _stream(stream, q.device)), "paged_attention_decode_noalloc")
 
 
 def copy_blocks(k_pools: Sequence, v_pools: Sequence, pairs, *, stream=None) -> None:

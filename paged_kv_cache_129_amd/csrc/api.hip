@@ -6,6 +6,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
+#include <map>
+#include <mutex>
 
 #include "kernels.h"
 #include "pa_device.h"
@@ -157,7 +159,43 @@ size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, in
                          num_partitions(max_context_len, partition_size));
 }
 
-pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
+}  // extern "C"
+
+// Scratch of the allocation-free decode entry point (see scratch_ptr below).
+static __device__ __attribute__((aligned(256))) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+// ---------------------------------------------------------------- static scratch
+// The allocation-free decode entry point keeps its partial records and range
+// descriptors here: a file-scope device array, one copy per GPU, alive until
+// the process ends.  Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in symbol); it asks the runtime for the array's
+// address on each device once and uses that address.
+constexpr size_t kScratchBytes = (size_t)PA_NOALLOC_SCRATCH_BYTES;
+
+// Address of `scratch` on the current device (looked up once per device, with
+// that device current), or NULL if the runtime cannot give it.
+void* scratch_ptr() {
+    static std::mutex mu;
+    static std::map<int, void*> ptrs;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+    std::lock_guard<std::mutex> g(mu);
+    auto it = ptrs.find(dev);
+    if (it != ptrs.end()) return it->second;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+        snprintf(g_last_error, sizeof(g_last_error), "hipGetSymbolAddress(scratch): %s",
+                 hipGetErrorString(e));
+        return nullptr;
+    }
+    ptrs.emplace(dev, p);
+    return p;
+}
+
+pa_status decode_impl(void* out, const void* q, int32_t q_dtype,
                                     const void* k_pool, const void* v_pool, int32_t kv_dtype,
                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
                                     const int32_t* context_lens, int32_t max_context_len,
@@ -165,7 +203,7 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                     float scale, float k_scale, float v_scale,
                                     int32_t partition_size, void* workspace,
-                                    size_t workspace_bytes, void* stream) {
+                                    size_t workspace_bytes, bool use_scratch, void* stream) {
     if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype)) return PA_ERR_INVALID_ARG;
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
@@ -192,14 +230,33 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
     const bool balanced = partition_size == PA_PARTITION_BALANCED;
     const int64_t parts = balanced ? 1 : num_partitions(ctx_cap, partition_size);
     if ((int64_t)num_seqs * num_heads * parts >= ((int64_t)1 << 31)) return PA_ERR_UNSUPPORTED;
-    const size_t rec_bytes =
+    size_t rec_bytes =
         balanced ? balanced_record_bytes(num_seqs, unit_group(num_heads, num_kv_heads), head_dim)
                  : partial_bytes(num_seqs, num_heads, head_dim, parts);
-    const size_t need =
-        rec_bytes + (balanced ? balanced_desc_bytes(num_seqs) : 0);
-    if (need > 0 && (!workspace || workspace_bytes < need ||
-                     (reinterpret_cast<uintptr_t>(workspace) & 255u)))
-        return PA_ERR_WORKSPACE;
+    int64_t rec_capacity = -1;                            // records: sized for any grid
+    if (use_scratch) {
+        // the library's own per-device scratch: records from its start, the
+        // balanced split's range descriptors at its end; the balanced records
+        // are checked against what remains once the grid is known
+        if (!rec_bytes && !balanced) {
+            workspace = nullptr;
+        } else {
+            workspace = scratch_ptr();
+            if (!workspace) return PA_ERR_HIP;
+            const size_t desc_bytes = balanced ? balanced_desc_bytes(num_seqs) : 0;
+            if (desc_bytes >= kScratchBytes || (!balanced && rec_bytes > kScratchBytes))
+                return PA_ERR_WORKSPACE;
+            if (balanced) {
+                rec_bytes = kScratchBytes - desc_bytes;
+                rec_capacity = (int64_t)(rec_bytes / ((size_t)(head_dim + 2) * sizeof(float)));
+            }
+        }
+    } else {
+        const size_t need = rec_bytes + (balanced ? balanced_desc_bytes(num_seqs) : 0);
+        if (need > 0 && (!workspace || workspace_bytes < need ||
+                         (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+            return PA_ERR_WORKSPACE;
+    }
 
     pa::DecodeArgs a{};
     a.q = q;
@@ -210,6 +267,7 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
     a.ctx_lens = context_lens;
     a.ws = reinterpret_cast<float*>(workspace);
     a.nrec = (int64_t)num_seqs * num_heads * parts;     // balanced: set with the grid
+    a.rec_capacity = rec_capacity;
     a.desc = balanced ? reinterpret_cast<int64_t*>(reinterpret_cast<char*>(workspace) + rec_bytes)
                       : nullptr;
     a.num_seqs = num_seqs;
@@ -225,8 +283,46 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
     const float vfac = kv_dtype == PA_FP8_E4M3 ? v_scale * pa::dequant_factor(kv_dtype) : 1.0f;
     a.qk_scale = scale * pa::kLog2e * kfac;
     a.out_scale = vfac;
-    return launch_checked(
+    const pa_status st = launch_checked(
         [&] { return pa::launch_decode(a, q_dtype, kv_dtype, head_dim, as_stream(stream)); });
+    // the records of the chosen grid did not fit the scratch (nothing launched)
+    if (st == PA_ERR_HIP && rec_capacity >= 0 && a.nrec > rec_capacity) return PA_ERR_WORKSPACE;
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
+                                    const void* k_pool, const void* v_pool, int32_t kv_dtype,
+                                    const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                    const int32_t* context_lens, int32_t max_context_len,
+                                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                    float scale, float k_scale, float v_scale,
+                                    int32_t partition_size, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, num_seqs, num_heads, num_kv_heads, head_dim,
+                       block_size, num_blocks, scale, k_scale, v_scale, partition_size, workspace,
+                       workspace_bytes, false, stream);
+}
+
+pa_status pa_paged_attention_decode_noalloc(void* out, const void* q, int32_t q_dtype,
+                                            const void* k_pool, const void* v_pool,
+                                            int32_t kv_dtype, const int32_t* block_tables,
+                                            int32_t max_blocks_per_seq,
+                                            const int32_t* context_lens, int32_t max_context_len,
+                                            int32_t num_seqs, int32_t num_heads,
+                                            int32_t num_kv_heads, int32_t head_dim,
+                                            int32_t block_size, int32_t num_blocks, float scale,
+                                            float k_scale, float v_scale, int32_t partition_size,
+                                            void* stream) {
+    return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, num_seqs, num_heads, num_kv_heads, head_dim,
+                       block_size, num_blocks, scale, k_scale, v_scale, partition_size, nullptr, 0,
+                       true, stream);
 }
 
 pa_status pa_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,

@@ -394,6 +394,7 @@ hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
     a.seg_cost = 16;                                    // an item start, in tokens (measured)
     a.units_per_kv = a.num_heads / a.num_kv_heads;
     const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), NW * 64, a.num_heads, 1, a);
+    if (grid < 0) return hipErrorOutOfMemory;
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }
@@ -501,6 +502,7 @@ int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers
         grid = persistent_grid(kernel, threads, (int64_t)device_cus() * kMaxWorkersPerCu / per_wg);
         const int64_t windows = (a.num_seqs + kWindow - 1) / kWindow;
         a.nrec = windows * grid * per_wg * 2 * a.unit_heads;
+        if (a.rec_capacity >= 0 && a.nrec > a.rec_capacity) return -1;
     } else {
         grid = persistent_grid(kernel, threads, ((int64_t)a.num_seqs * units * a.num_parts + per_wg - 1) / per_wg);
     }

@@ -528,6 +528,7 @@ hipError_t launch_tiles(DecodeArgs& a, hipStream_t stream) {
     a.units_per_kv = (G + a.unit_heads - 1) / a.unit_heads;
     const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), NW * 64,
                                      a.num_kv_heads * a.units_per_kv, 1, a);
+    if (grid < 0) return hipErrorOutOfMemory;
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
 }

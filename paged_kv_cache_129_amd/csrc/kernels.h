@@ -72,6 +72,7 @@ struct DecodeArgs {
     const int32_t* ctx_lens;
     float* ws;                  // partial records: m[nrec], l[nrec], o[nrec][head_dim]
     int64_t nrec;               // partial records in ws (set with the grid when balanced)
+    int64_t rec_capacity;       // balanced: records ws can hold, or -1 (sized for any grid)
     int64_t* desc;              // balanced: kDescWords per (window, worker) for the reduction
     int32_t units;              // work units per sequence (set at launch): a unit is
                                 // unit_heads query heads of KV head unit / units_per_kv,
@@ -100,7 +101,8 @@ int device_cus();
 // Grid of an attention launch with `units` work units per sequence (unit_heads
 // and units_per_kv already set), whose workers are wavefronts (wave_workers) or
 // workgroups; records the worker count (and, when balanced, the partial-record
-// count) in `a`.
+// count) in `a`.  Returns -1 when the balanced records would not fit
+// a.rec_capacity (the launcher then returns hipErrorOutOfMemory unlaunched).
 int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers, DecodeArgs& a);
 hipError_t launch_decode(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                          hipStream_t stream);
