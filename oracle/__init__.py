@@ -14,6 +14,9 @@ What it computes is the plain definition, in float64, written from the pages:
   fetches K/V block by block through the block table (KV 缓存与分页注意力
   §07), so the oracle first gathers each sequence's tokens through its block
   table into contiguous arrays and then applies the textbook formula.
+* multi-token attention for the prompt phase and chunked prefill: each new
+  token's query attends over the cached tokens up to and including its own
+  position (KV 缓存与分页注意力 §02; KV Cache从原理到实战 §2.3, §5.4);
 * the cache write, the copy-on-write block copy, the host block allocator
   (free list, reference counts, copy-on-write; KV 缓存与分页注意力 §07–§08,
   KV Cache从原理到实战 §6.2), the per-token KV size (§03 / §2.2), and the
@@ -26,5 +29,6 @@ library routines.  Nothing here is "parity unpinned".
 from .formats import (decode, e4m3_decode_table, e4m3_encode, e4m3_values)  # noqa: F401
 from .attention import (gather_sequence, paged_attention, contiguous_attention,  # noqa: F401
                         partition_states, lse_combine, kv_write, copy_blocks)
+from .prefill import paged_prefill, query_positions  # noqa: F401
 from .allocator import Allocator, OutOfBlocks, UnknownSequence, RefcountError  # noqa: F401
 from .sizes import kv_bytes_per_token  # noqa: F401

@@ -449,3 +449,118 @@ def device_pool_case(name: str, config: str, *, num_seqs: int, num_heads: int, n
     return dict(name=name, k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new, q=q,
                 tables=tables, ctx=ctx, slots=slots, num_heads=H, num_kv_heads=Hkv, head_dim=D,
                 block_size=bs, num_blocks=num_blocks, kv_dtype=kv_dtype, scale=1.0 / math.sqrt(D))
+
+
+# ---------------------------------------------------------------- multi-token (prefill) cases
+@dataclasses.dataclass
+class PrefillCase:
+    """One layer's chunked-prefill step: pools holding each sequence's earlier
+    tokens, the chunk's new K/V (written through their slots before attention)
+    and the chunk's queries, packed row after row.
+
+    ``context_lens`` count the chunk; sequence s's query rows are
+    ``query_start[s]:query_start[s+1]`` and belong to its last
+    ``query_start[s+1] - query_start[s]`` positions.
+    """
+    name: str
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    kv_dtype: str
+    q_dtype: str
+    context_lens: np.ndarray          # int32 [S], chunk included
+    query_start: np.ndarray           # int32 [S + 1]
+    block_tables: np.ndarray          # int32 [S, MB], -1 padded
+    k_pool: np.ndarray                # storage [NB, Hkv, bs, D] (before the chunk's write)
+    v_pool: np.ndarray
+    k_new: np.ndarray                 # q_dtype storage [T, Hkv, D]
+    v_new: np.ndarray
+    slot_mapping: np.ndarray          # int64 [T]
+    q: np.ndarray                     # q_dtype storage [T, H, D]
+    scale: float
+    k_scale: float = 1.0
+    v_scale: float = 1.0
+
+    @property
+    def num_tokens(self) -> int:
+        return int(self.query_start[-1])
+
+    @property
+    def max_query_len(self) -> int:
+        return int(np.diff(self.query_start).max(initial=0))
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max(initial=0))
+
+
+def make_prefill_case(name: str, config: str, *, prior_lens: Sequence[int],
+                      chunk_lens: Sequence[int], num_heads: int, num_kv_heads: int,
+                      head_dim: int, block_size: int, kv_dtype: str, q_dtype: str,
+                      num_blocks: Optional[int] = None, spare_blocks: int = 0,
+                      value_scale: float = 1.0, layer: int = 0, salt: int = 0) -> PrefillCase:
+    """Sequences with ``prior_lens[s]`` tokens already cached and a chunk of
+    ``chunk_lens[s]`` new tokens; shuffled placement, N(0,1)*value_scale values,
+    NaN poison in every slot no earlier token owns (the chunk's slots included,
+    until the write)."""
+    prior = np.asarray(prior_lens, dtype=np.int64)
+    chunk = np.asarray(chunk_lens, dtype=np.int64)
+    S, H, Hkv, D, bs = len(prior), num_heads, num_kv_heads, head_dim, block_size
+    assert chunk.shape == (S,) and H % Hkv == 0
+    ctx = (prior + chunk).astype(np.int32)
+    nbs = blocks_needed(ctx, bs)
+    NB = int(nbs.sum()) + spare_blocks if num_blocks is None else num_blocks
+    tables = place_blocks(rng_for(config, layer, "place", 100 + salt), NB, nbs)
+    rk, rv = rng_for(config, layer, "k", 100 + salt), rng_for(config, layer, "v", 100 + salt)
+    k_vals = [rk.standard_normal((int(n), Hkv, D), dtype=np.float32) * np.float32(value_scale)
+              for n in prior]
+    v_vals = [rv.standard_normal((int(n), Hkv, D), dtype=np.float32) * np.float32(value_scale)
+              for n in prior]
+    T = int(chunk.sum())
+    k_new32 = rng_for(config, layer, "knew", 100 + salt).standard_normal((T, Hkv, D), dtype=np.float32) \
+        * np.float32(value_scale)
+    v_new32 = rng_for(config, layer, "vnew", 100 + salt).standard_normal((T, Hkv, D), dtype=np.float32) \
+        * np.float32(value_scale)
+    q32 = rng_for(config, layer, "q", 100 + salt).standard_normal((T, H, D), dtype=np.float32) \
+        * np.float32(value_scale)
+    k_new, v_new, q = (to_storage(x, q_dtype) for x in (k_new32, v_new32, q32))
+    k_scale = v_scale = 1.0
+    if kv_dtype == "fp8_e4m3":
+        def amax(vals, new):
+            m = float(np.abs(storage_to_f32(new, q_dtype)).max(initial=0.0))
+            for a in vals:
+                if a.size:
+                    m = max(m, float(np.abs(a).max()))
+            return m
+        k_scale = float(np.float32(max(amax(k_vals, k_new), 1e-30) / 448.0))
+        v_scale = float(np.float32(max(amax(v_vals, v_new), 1e-30) / 448.0))
+    k_pool = empty_pool(NB, Hkv, bs, D, kv_dtype)
+    v_pool = empty_pool(NB, Hkv, bs, D, kv_dtype)
+    for s in range(S):
+        fill_tokens(k_pool, tables[s], to_storage(k_vals[s], kv_dtype, k_scale), bs)
+        fill_tokens(v_pool, tables[s], to_storage(v_vals[s], kv_dtype, v_scale), bs)
+    query_start = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int32)
+    slots = np.empty(T, dtype=np.int64)
+    for s in range(S):
+        pos = prior[s] + np.arange(chunk[s])
+        slots[query_start[s]:query_start[s + 1]] = \
+            tables[s, pos // bs].astype(np.int64) * bs + pos % bs
+    return PrefillCase(name=name, num_seqs=S, num_heads=H, num_kv_heads=Hkv, head_dim=D,
+                       block_size=bs, num_blocks=NB, kv_dtype=kv_dtype, q_dtype=q_dtype,
+                       context_lens=ctx, query_start=query_start, block_tables=tables,
+                       k_pool=k_pool, v_pool=v_pool, k_new=k_new, v_new=v_new,
+                       slot_mapping=slots, q=q, scale=1.0 / math.sqrt(D), k_scale=k_scale,
+                       v_scale=v_scale)
+
+
+def llama7b_prefill_case(num_seqs: int = 8, chunk: int = 512, layer: int = 0) -> PrefillCase:
+    """Llama-2-7B-shaped chunked prefill: 32 heads x 128, fp16, block 16; sequence s
+    has s * 512 tokens cached and a 512-token chunk, so contexts run 512..4096."""
+    prior = [chunk * s for s in range(num_seqs)]
+    return make_prefill_case("llama7b_prefill", "llama7b", prior_lens=prior,
+                             chunk_lens=[chunk] * num_seqs, num_heads=32, num_kv_heads=32,
+                             head_dim=128, block_size=16, kv_dtype="f16", q_dtype="f16",
+                             spare_blocks=64, layer=layer)
