@@ -172,6 +172,46 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
                                     int32_t partition_size, void* workspace,
                                     size_t workspace_bytes, void* stream);
 
+/*
+ * paged_attention_prefill — multi-token attention over a paged cache: the
+ * prompt phase, or one chunk of a chunked prefill.  The prompt phase handles
+ * a whole prompt at once (KV 缓存与分页注意力 §02); it is compute-bound where
+ * decode is bandwidth-bound, and a long prompt may be cut into chunks so that
+ * its prefill does not hold up decoding (KV Cache从原理到实战 §2.3, §5.4).
+ * Write the chunk's K/V with pa_kv_cache_write first (one slot per new
+ * token), then call this: every token is read through the block table.
+ *
+ * For sequence s with n = context_lens[s] tokens (the chunk included) and the
+ * q_len = query_start[s+1] - query_start[s] query rows query_start[s] + i,
+ * row i sits at position p = n - q_len + i and, for each head h with
+ * g = h / (num_heads / num_kv_heads):
+ *     out[row][h] = sum_{t <= p} softmax_t(scale * q[row][h] . K_s[t][g]) * V_s[t][g]
+ * (causal over the new tokens; every earlier token is visible).  Rows with
+ * p < 0 (a chunk longer than its context) give zeros.
+ *
+ *   out, q          DEVICE [num_query_tokens][num_heads][head_dim], q_dtype
+ *   k_pool, v_pool  DEVICE, pool layout above; kv_dtype == q_dtype in {F16, BF16}
+ *                   (other pairs: PA_ERR_UNSUPPORTED)
+ *   block_tables    DEVICE int32 [num_seqs][max_blocks_per_seq]; an entry
+ *                   outside [0, num_blocks) makes its tokens absent
+ *   context_lens    DEVICE int32 [num_seqs], clamped to [0, max_blocks_per_seq * block_size]
+ *   query_start     DEVICE int32 [num_seqs + 1], non-decreasing row offsets
+ *                   (values are clamped to [0, num_query_tokens])
+ *   max_query_len   host-known bound of every q_len (sizes the launch); rows of
+ *                   a sequence beyond it are not written
+ *   scale           softmax scale (1/sqrt(head_dim) for standard attention)
+ * Limits: head_dim in {64, 128}; block_size a power of two in [1, 256];
+ * num_heads % num_kv_heads == 0.  No workspace; nothing is allocated.
+ */
+pa_status pa_paged_attention_prefill(void* out, const void* q, int32_t q_dtype,
+                                     const void* k_pool, const void* v_pool, int32_t kv_dtype,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, const int32_t* query_start,
+                                     int32_t num_seqs, int32_t num_query_tokens,
+                                     int32_t max_query_len, int32_t num_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, float scale, void* stream);
+
 /* Size of the device scratch the allocation-free decode entry point uses
  * (one copy per GPU, held from the library's load until the process ends). */
 #define PA_NOALLOC_SCRATCH_BYTES (64u << 20)

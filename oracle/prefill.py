@@ -39,7 +39,8 @@ def query_positions(n: int, q_len: int) -> np.ndarray:
 def paged_prefill(q: np.ndarray, q_dtype: str, k_pool: np.ndarray, v_pool: np.ndarray,
                   kv_dtype: str, block_tables: np.ndarray, context_lens: Sequence[int],
                   query_start: Sequence[int], block_size: int, scale: float,
-                  k_scale: float = 1.0, v_scale: float = 1.0) -> np.ndarray:
+                  k_scale: float = 1.0, v_scale: float = 1.0,
+                  rows: Sequence[int] = None) -> np.ndarray:
     """Causal multi-token attention over a paged cache, float64 [T, H, D].
 
     ``q`` is [T, H, D] with the rows of sequence s at
@@ -47,20 +48,24 @@ def paged_prefill(q: np.ndarray, q_dtype: str, k_pool: np.ndarray, v_pool: np.nd
     tokens through its block table, keep those at positions <= the row's own
     position, and apply the decode definition (softmax of the scaled dot
     products, weighted sum of values; heads share KV groups as in decode).
+    ``rows`` restricts the work to some query rows (others stay zero).
     """
     Q = decode(q, q_dtype)
     T, H, D = Q.shape
     out = np.zeros((T, H, D), dtype=np.float64)
     qs = np.asarray(query_start, dtype=np.int64)
+    wanted = None if rows is None else set(int(r) for r in rows)
     for s in range(len(qs) - 1):
         r0, r1 = int(qs[s]), int(qs[s + 1])
         n = int(context_lens[s])
         if r1 <= r0 or n <= 0:
             continue
+        if wanted is not None and not any(r in wanted for r in range(r0, r1)):
+            continue
         K = gather_sequence(k_pool, kv_dtype, block_tables[s], n, block_size, k_scale)
         V = gather_sequence(v_pool, kv_dtype, block_tables[s], n, block_size, v_scale)
         for i, p in enumerate(query_positions(n, r1 - r0)):
-            if p < 0:
+            if p < 0 or (wanted is not None and r0 + i not in wanted):
                 continue
             out[r0 + i] = _attend_one(Q[r0 + i], K[:p + 1], V[:p + 1], scale)
     return out

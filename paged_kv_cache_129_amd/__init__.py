@@ -50,6 +50,10 @@ _SIGNATURES = [
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float, ctypes.c_float,
       ctypes.c_int32, _vp]),
+    ("pa_paged_attention_prefill", ctypes.c_int32,
+     [_vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, _vp]),
     ("pa_copy_blocks", ctypes.c_int32,
      [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
@@ -225,6 +229,33 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, *
         block_tables.shape[1], _dev(context_lens, "context_lens"), int(max_context_len), S, H,
         Hkv, D, bs, NB, float(scale), float(k_scale), float(v_scale), int(partition_size),
         ws_ptr, ws_bytes, _stream(stream, q.device)), "paged_attention_decode")
+
+
+def paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start, *,
+                            max_query_len: int, scale: float, stream=None) -> None:
+    """out[T, H, D] = causal multi-token attention of q[T, H, D] (rows of sequence s
+    at query_start[s]:query_start[s+1], the last rows of its context) over paged
+    [NB, Hkv, bs, D] pools."""
+    torch = _torch()
+    T, H, D = q.shape
+    NB, Hkv, bs, D2 = k_pool.shape
+    S = context_lens.shape[0]
+    if D2 != D or out.shape != q.shape or out.dtype != q.dtype or v_pool.shape != k_pool.shape:
+        raise ValueError("shape mismatch")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [S, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.dim() != 1:
+        raise ValueError("context_lens must be int32 [S]")
+    if query_start.dtype != torch.int32 or query_start.shape != (S + 1,):
+        raise ValueError("query_start must be int32 [S + 1]")
+    _same_dtype(k_pool, v_pool, "k_pool", "v_pool")
+    _one_device(out, q, k_pool, v_pool, block_tables, context_lens, query_start)
+    _check(lib.pa_paged_attention_prefill(
+        _dev(out, "out"), _dev(q, "q"), dtype_code(q), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"), dtype_code(k_pool), _dev(block_tables, "block_tables"),
+        block_tables.shape[1], _dev(context_lens, "context_lens"), _dev(query_start, "query_start"),
+        S, T, int(max_query_len), H, Hkv, D, bs, NB, float(scale), _stream(stream, q.device)),
+        "paged_attention_prefill")
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20

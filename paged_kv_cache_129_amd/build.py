@@ -20,7 +20,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
-HIP_SOURCES = ["api.hip", "kv_write.hip", "copy_blocks.hip", "decode.hip", "decode_mfma.hip"]
+HIP_SOURCES = ["api.hip", "kv_write.hip", "copy_blocks.hip", "decode.hip", "decode_mfma.hip",
+               "prefill_mfma.hip"]
 HOST_SOURCES = ["allocator.cpp"]
 ARCH = "gfx950"
 

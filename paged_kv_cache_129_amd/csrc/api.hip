@@ -325,6 +325,50 @@ pa_status pa_paged_attention_decode_noalloc(void* out, const void* q, int32_t q_
                        true, stream);
 }
 
+pa_status pa_paged_attention_prefill(void* out, const void* q, int32_t q_dtype,
+                                     const void* k_pool, const void* v_pool, int32_t kv_dtype,
+                                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, const int32_t* query_start,
+                                     int32_t num_seqs, int32_t num_query_tokens,
+                                     int32_t max_query_len, int32_t num_heads,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, float scale, void* stream) {
+    if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype)) return PA_ERR_INVALID_ARG;
+    if (num_seqs < 0 || num_query_tokens < 0 || max_query_len < 0 || num_heads <= 0 ||
+        num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (num_heads % num_kv_heads != 0) return PA_ERR_INVALID_ARG;
+    const int lbs = log2_exact(block_size);
+    if (lbs < 0 || lbs > 8) return PA_ERR_INVALID_ARG;
+    if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
+    if (!pa::prefill_supported(q_dtype, kv_dtype, head_dim)) return PA_ERR_UNSUPPORTED;
+    if (num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0) return PA_OK;
+    if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_INVALID_ARG;
+    pa::PrefillArgs a{};
+    a.q = q;
+    a.out = out;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.tables = block_tables;
+    a.ctx_lens = context_lens;
+    a.query_start = query_start;
+    a.num_seqs = num_seqs;
+    a.num_tokens = num_query_tokens;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_blocks = num_blocks;
+    a.log2_bs = lbs;
+    a.max_query_len = max_query_len;
+    a.qk_scale = scale * pa::kLog2e;
+    a.out_scale = 1.0f;
+    return launch_checked(
+        [&] { return pa::launch_prefill(a, q_dtype, kv_dtype, head_dim, as_stream(stream)); });
+}
+
 pa_status pa_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num_layers,
                          int32_t kv_dtype, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t num_blocks, const int32_t* pairs,

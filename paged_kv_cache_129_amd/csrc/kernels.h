@@ -107,6 +107,32 @@ int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers
 hipError_t launch_decode(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                          hipStream_t stream);
 
+// Multi-token (prefill / chunked prefill) attention, matrix-core kernel
+// (prefill_mfma.hip).  Columns of a (sequence, KV head) item are the pairs
+// (query row i, head hl of the KV head's group), column c = i * G + hl.
+struct PrefillArgs {
+    const void* q;              // [num_query_tokens][num_heads][head_dim]
+    void* out;
+    const void* k_pool;
+    const void* v_pool;
+    const int32_t* tables;      // [num_seqs][max_blocks]
+    const int32_t* ctx_lens;    // [num_seqs], chunk included
+    const int32_t* query_start; // [num_seqs + 1]
+    int32_t num_seqs;
+    int32_t num_tokens;         // rows of q / out
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    int32_t max_blocks;
+    int32_t num_blocks;
+    int32_t log2_bs;
+    int32_t max_query_len;      // rows per sequence the launch covers
+    int32_t col_blocks;         // column blocks per (sequence, KV head) (set at launch)
+    float qk_scale;             // softmax scale * log2(e) * K dequant factor
+    float out_scale;            // V dequant factor
+};
+bool prefill_supported(int q_dt, int kv_dt, int head_dim);
+hipError_t launch_prefill(PrefillArgs& a, int q_dt, int kv_dt, int head_dim, hipStream_t stream);
+
 // matrix-core kernel for grouped heads, 2 <= G <= kMaxGroup (decode_mfma.hip)
 bool decode_mfma_supported(int q_dt, int kv_dt, int head_dim, int group);
 hipError_t launch_decode_mfma(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,

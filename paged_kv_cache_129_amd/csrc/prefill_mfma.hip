@@ -1,0 +1,314 @@
+// Multi-token paged attention (prompt phase, chunked prefill), matrix-core
+// kernel for gfx950.
+//
+// The prompt phase computes a whole prompt at once (KV 缓存与分页注意力 §02);
+// it is compute-bound where decode is bandwidth-bound (KV Cache从原理到实战
+// §2.3), and a long prompt may be cut into chunks (§5.4).  The chunk's K/V
+// are written into the paged pool first (kv_cache_write); this kernel then
+// reads every token through the block table.  Query row i of a sequence with
+// n cached tokens and a q_len-row chunk sits at position p = n - q_len + i and
+// attends over tokens 0..p (a causal mask over the new tokens).
+//
+// Work split.  An item is (sequence, KV head, column block): the columns of
+// a (sequence, KV head) are the pairs (query row i, head hl of the KV head's
+// group of G), c = i * G + hl, so grouped heads and query rows fill the same
+// matrix dimension.  A workgroup of NW wavefronts owns NW * TQ * 16 columns
+// (TQ 16-column tiles per wavefront) and streams the K/V tokens 0..p_last of
+// its last column in chunks of kKT tokens.  Each chunk is loaded once per
+// workgroup (16-byte global loads, one chunk ahead in registers, block ids
+// two chunks ahead) into double-buffered LDS tiles; every wavefront then runs
+// on its own columns, per 16-token sub-chunk:
+//   * S^T[token][column] = K · Q^T on v_mfma_f32_16x16x32 (K from LDS as the
+//     A operand, row = token; the wavefront's queries stay in registers as B);
+//   * the online softmax per column (running maximum in log2 units, moved only
+//     when a score passes it by more than kMaxSlack, so rescales are rare);
+//   * O^T[d][column] += V^T · P^T on v_mfma_f32_16x16x16, V^T read from the
+//     LDS tile with the transposing ds_read_b64_tr_b16, P^T being the score
+//     result's own register layout (bf16: P split into two bf16 parts).
+// Sub-chunks past a tile's last position are skipped; only sub-chunks that
+// reach past a tile's first position need the causal mask.  Tokens with an
+// invalid block id count as absent (their V rows are zeroed in LDS).
+#include "kernels.h"
+#include "mfma_util.h"
+#include "pa_device.h"
+
+namespace pa {
+namespace {
+
+constexpr int kKT = 64;             // tokens per staged K/V chunk
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kMaxSlack = 8.0f;   // log2 units a score may exceed the reference maximum by
+
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+template <int DT, int D, int NW, int TQ, int WPE>
+__global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs a) {
+    constexpr int NC = D / 32;          // score MFMAs per sub-chunk and tile
+    constexpr int NDT = D / 16;         // output d-tiles
+    constexpr int LDK = D + 8;          // K tile row stride (halfs): 16 rows of a
+                                        // 16-byte column read hit distinct banks
+    constexpr int LDV = D + 16;         // V tile row stride (halfs): conflict-free
+                                        // transposed reads
+    constexpr int PPR = D * 2 / 16;     // 16-byte pieces per token row
+    constexpr int NT = NW * 64;
+    constexpr int PPT = kKT * PPR / NT; // pieces per thread per tensor and chunk
+    constexpr int CB = NW * TQ * 16;    // columns per workgroup
+    static_assert(PPT * NT == kKT * PPR, "chunk split");
+
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKT * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[2][kKT * LDV];
+    __shared__ __attribute__((aligned(4))) uint8_t live_s[2][kKT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int j = lane >> 4;
+    const int c16 = lane & 15;
+    const int G = a.num_heads / a.num_kv_heads;
+    const int bs = 1 << a.log2_bs;
+
+    // item: KV head fastest, then sequence, then column block (last blocks first)
+    int bid = blockIdx.x;
+    const int g = bid % a.num_kv_heads;
+    bid /= a.num_kv_heads;
+    const int s = bid % a.num_seqs;
+    const int cb = a.col_blocks - 1 - bid / a.num_seqs;
+    const int r0 = clampi(a.query_start[s], 0, a.num_tokens);
+    const int r1 = clampi(a.query_start[s + 1], r0, a.num_tokens);
+    const int q_len = min(r1 - r0, a.max_query_len);
+    const int ncols = q_len * G;
+    const int c_first = cb * CB;
+    if (c_first >= ncols) return;                       // uniform over the workgroup
+    const int n = clampi(a.ctx_lens[s], 0, a.max_blocks << a.log2_bs);
+    const int pos0 = n - q_len;                         // position of query row 0
+    const int c_last = min(c_first + CB, ncols) - 1;
+    const int kv_end = clampi(pos0 + c_last / G + 1, 0, n);   // tokens the workgroup reads
+    const int nchunks = (kv_end + kKT - 1) / kKT;
+    const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
+
+    // ---- this wavefront's columns: per tile, the lane's column and its position
+    const int cw0 = c_first + wave * TQ * 16;
+    int pcol[TQ];                 // position of the lane's column (-1: none visible)
+    int pt_min[TQ], pt_max[TQ];   // first / last position of a tile's valid columns
+    Op8 qop[TQ][NC];
+#pragma unroll
+    for (int tt = 0; tt < TQ; ++tt) {
+        const int c = cw0 + 16 * tt + c16;
+        const bool valid = c < ncols;
+        pcol[tt] = valid ? pos0 + c / G : -1;
+        const int ct0 = cw0 + 16 * tt, ct1 = min(cw0 + 16 * tt + 15, ncols - 1);
+        pt_min[tt] = pos0 + ct0 / G;
+        pt_max[tt] = ct0 <= ct1 ? min(pos0 + ct1 / G, kv_end - 1) : -1;
+        const int i = valid ? c / G : 0, hl = valid ? c % G : 0;
+        const char* qrow = reinterpret_cast<const char*>(a.q) +
+                           (((int64_t)(r0 + i) * a.num_heads + g * G + hl) * D) * 2;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+            const Raw16 r = load16(qrow + (32 * cc + 8 * j) * 2);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) qop[tt][cc].w[w] = valid ? r.w[w] : 0u;
+        }
+    }
+    int p_wave_max = -1;
+#pragma unroll
+    for (int tt = 0; tt < TQ; ++tt) p_wave_max = max(p_wave_max, pt_max[tt]);
+
+    // ---- chunk loader: thread piece k is row (tid + k*NT) / PPR, 16-byte piece (tid % PPR)
+    const char* kbase = reinterpret_cast<const char*>(a.k_pool);
+    const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+    constexpr int64_t row_bytes = (int64_t)D * 2;
+    const int prow = tid / PPR;                          // first row of this thread
+    const int pcolb = (tid % PPR) * 16;                  // byte offset in the row
+    constexpr int RSTEP = NT / PPR;                      // rows between a thread's pieces
+    int blk_next[PPT];                                   // block ids of the next chunk's rows
+    auto load_table = [&](int ci) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int t = ci * kKT + prow + k * RSTEP;
+            blk_next[k] = t < kv_end ? trow[t >> a.log2_bs] : -1;
+        }
+    };
+    Raw16 kraw[PPT], vraw[PPT];
+    bool tlive[PPT];
+    auto load_data = [&](int ci) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int t = ci * kKT + prow + k * RSTEP;
+            const int b = blk_next[k];
+            tlive[k] = t < kv_end && b >= 0 && b < a.num_blocks;
+            const int64_t row = tlive[k]
+                ? (((int64_t)b * a.num_kv_heads + g) << a.log2_bs) + (t & (bs - 1)) : 0;
+            kraw[k] = load16_stream(kbase + row * row_bytes + pcolb);
+            vraw[k] = load16_stream(vbase + row * row_bytes + pcolb);
+        }
+    };
+    auto store_chunk = [&](int buf) {
+#pragma unroll
+        for (int k = 0; k < PPT; ++k) {
+            const int r = prow + k * RSTEP;
+            uint16_t* kd = &ks[buf][r * LDK + pcolb / 2];
+            uint16_t* vd = &vs[buf][r * LDV + pcolb / 2];
+            *reinterpret_cast<uint4*>(kd) = make_uint4(kraw[k].w[0], kraw[k].w[1], kraw[k].w[2], kraw[k].w[3]);
+            const bool lv = tlive[k];
+            *reinterpret_cast<uint4*>(vd) = lv ? make_uint4(vraw[k].w[0], vraw[k].w[1], vraw[k].w[2], vraw[k].w[3])
+                                               : make_uint4(0u, 0u, 0u, 0u);
+            if (pcolb == 0) live_s[buf][r] = lv ? 1 : 0;
+        }
+    };
+
+    float m[TQ], l[TQ];
+    f32x4 acc[TQ][NDT];
+#pragma unroll
+    for (int tt = 0; tt < TQ; ++tt) {
+        m[tt] = kNegInf;
+        l[tt] = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    if (nchunks > 0) {
+        load_table(0);
+        load_data(0);
+        if (nchunks > 1) load_table(1);
+    }
+    for (int ci = 0; ci < nchunks; ++ci) {
+        const int buf = ci & 1;
+        store_chunk(buf);
+        __syncthreads();
+        if (ci + 1 < nchunks) {
+            load_data(ci + 1);
+            if (ci + 2 < nchunks) load_table(ci + 2);
+        }
+        const int t0 = ci * kKT;
+        const uint16_t* kt = ks[buf];
+        const uint16_t* vt = vs[buf];
+#pragma unroll
+        for (int sub = 0; sub < kKT / 16; ++sub) {
+            const int u0 = t0 + 16 * sub;
+            if (u0 > p_wave_max) break;                  // uniform: nothing visible from here on
+            // K operands (A of the score MFMA): lane = token row, 8 head_dim numbers
+            Op8 kop[NC];
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc) {
+                const uint4 r = *reinterpret_cast<const uint4*>(&kt[(16 * sub + c16) * LDK + 32 * cc + 8 * j]);
+                kop[cc].w[0] = r.x;
+                kop[cc].w[1] = r.y;
+                kop[cc].w[2] = r.z;
+                kop[cc].w[3] = r.w;
+            }
+            const uint32_t lv4 = *reinterpret_cast<const uint32_t*>(&live_s[buf][16 * sub + 4 * j]);
+            Op4 pop[TQ], plo[TQ];
+            bool tile_on[TQ];
+#pragma unroll
+            for (int tt = 0; tt < TQ; ++tt) {
+                tile_on[tt] = u0 <= pt_max[tt];          // uniform
+                if (!tile_on[tt]) continue;
+                f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int cc = 0; cc < NC; ++cc) sc = mma32<DT>(kop[cc], qop[tt][cc], sc);
+                // causal mask only where the sub-chunk reaches past the tile's first position
+                const bool need_mask = u0 + 15 > pt_min[tt];
+                float sv[4];
+                bool live[4];
+                float mx = kNegInf;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = u0 + 4 * j + i;
+                    live[i] = ((lv4 >> (8 * i)) & 1u) && (!need_mask || t <= pcol[tt]);
+                    sv[i] = live[i] ? sc[i] * a.qk_scale : kNegInf;
+                    mx = fmaxf(mx, sv[i]);
+                }
+                mx = max_over_groups(mx);
+                const float mn = (mx > m[tt] + kMaxSlack) ? mx : m[tt];
+                const bool moved = mn != m[tt];
+                const float alpha = moved ? fast_exp2(m[tt] - mn) : 1.0f;
+                float pr[4];
+                float psum = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pr[i] = live[i] ? fast_exp2(sv[i] - mn) : 0.0f;
+                    psum += pr[i];
+                }
+                l[tt] = l[tt] * alpha + psum;
+                m[tt] = mn;
+                if (__builtin_amdgcn_ballot_w64(moved)) {
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] *= alpha;
+                }
+                pop[tt].w[0] = pack2<DT>(pr[0], pr[1]);
+                pop[tt].w[1] = pack2<DT>(pr[2], pr[3]);
+                if constexpr (DT == PA_BF16) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const float h0 = __uint_as_float(pop[tt].w[q] << 16);
+                        const float h1 = __uint_as_float(pop[tt].w[q] & 0xFFFF0000u);
+                        plo[tt].w[q] = pack2<DT>(pr[2 * q] - h0, pr[2 * q + 1] - h1);
+                    }
+                }
+            }
+            // O^T[d][column] += V^T[d][token] · P^T[token][column], V^T read transposed
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const Op4 vop = read_tr16(&vt[(16 * sub + 4 * j + (c16 >> 2)) * LDV + 16 * dt + 4 * (c16 & 3)]);
+#pragma unroll
+                for (int tt = 0; tt < TQ; ++tt) {
+                    if (!tile_on[tt]) continue;
+                    acc[tt][dt] = mma16<DT>(vop, pop[tt], acc[tt][dt]);
+                    if constexpr (DT == PA_BF16) acc[tt][dt] = mma16<DT>(vop, plo[tt], acc[tt][dt]);
+                }
+            }
+        }
+        // no barrier here: the next chunk goes into the other buffer, and the
+        // barrier after that store orders this chunk's reads before the buffer
+        // is written again
+    }
+
+    // ---- normalise and store: lane holds column c16 of each tile, d = 16 dt + 4 j .. + 3
+#pragma unroll
+    for (int tt = 0; tt < TQ; ++tt) {
+        const float lt = sum_over_groups(l[tt]);
+        const int c = cw0 + 16 * tt + c16;
+        if (c < ncols) {
+            const int i = c / G, hl = c % G;
+            const float f = (lt > 0.0f ? 1.0f / lt : 0.0f) * a.out_scale;
+            char* orow = reinterpret_cast<char*>(a.out) +
+                         (((int64_t)(r0 + i) * a.num_heads + g * G + hl) * D) * 2;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const int d = 16 * dt + 4 * j;
+                *reinterpret_cast<uint2*>(orow + d * 2) =
+                    make_uint2(pack2<DT>(acc[tt][dt][0] * f, acc[tt][dt][1] * f),
+                               pack2<DT>(acc[tt][dt][2] * f, acc[tt][dt][3] * f));
+            }
+        }
+    }
+}
+
+template <int DT, int D>
+hipError_t launch_typed(PrefillArgs& a, hipStream_t stream) {
+    constexpr int NW = 4, TQ = 2, WPE = 2;
+    constexpr int CB = NW * TQ * 16;
+    const int G = a.num_heads / a.num_kv_heads;
+    a.col_blocks = (int32_t)(((int64_t)a.max_query_len * G + CB - 1) / CB);
+    const int64_t grid = (int64_t)a.col_blocks * a.num_seqs * a.num_kv_heads;
+    if (grid <= 0) return hipSuccess;
+    if (grid > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((prefill_mfma_kernel<DT, D, NW, TQ, WPE>), dim3((uint32_t)grid), dim3(NW * 64),
+                       0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_supported(int q_dt, int kv_dt, int head_dim) {
+    return (head_dim == 64 || head_dim == 128) && q_dt == kv_dt && (q_dt == PA_F16 || q_dt == PA_BF16);
+}
+
+hipError_t launch_prefill(PrefillArgs& a, int q_dt, int kv_dt, int head_dim, hipStream_t stream) {
+    if (!prefill_supported(q_dt, kv_dt, head_dim)) return hipErrorInvalidValue;
+    if (q_dt == PA_F16) return head_dim == 64 ? launch_typed<PA_F16, 64>(a, stream)
+                                              : launch_typed<PA_F16, 128>(a, stream);
+    return head_dim == 64 ? launch_typed<PA_BF16, 64>(a, stream) : launch_typed<PA_BF16, 128>(a, stream);
+}
+
+}  // namespace pa
