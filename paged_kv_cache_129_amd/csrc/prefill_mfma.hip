@@ -17,14 +17,15 @@
 // its last column in chunks of kKT tokens.  Each chunk is loaded once per
 // workgroup (16-byte global loads, one chunk ahead in registers, block ids
 // two chunks ahead) into double-buffered LDS tiles; every wavefront then runs
-// on its own columns, per 16-token sub-chunk:
+// on its own columns, 32 tokens at a time:
 //   * S^T[token][column] = K · Q^T on v_mfma_f32_16x16x32 (K from LDS as the
 //     A operand, row = token; the wavefront's queries stay in registers as B);
 //   * the online softmax per column (running maximum in log2 units, moved only
 //     when a score passes it by more than kMaxSlack, so rescales are rare);
-//   * O^T[d][column] += V^T · P^T on v_mfma_f32_16x16x16, V^T read from the
-//     LDS tile with the transposing ds_read_b64_tr_b16, P^T being the score
-//     result's own register layout (bf16: P split into two bf16 parts).
+//   * O^T[d][column] += V^T · P^T on v_mfma_f32_16x16x32 over two 16-token
+//     halves at once, V^T read from the LDS tile with the transposing
+//     ds_read_b64_tr_b16, P^T being the score results' own register layout
+//     (bf16: P split into two bf16 parts).
 // Sub-chunks past a tile's last position are skipped; only sub-chunks that
 // reach past a tile's first position need the causal mask.  Tokens with an
 // invalid block id count as absent (their V rows are zeroed in LDS).
@@ -109,9 +110,15 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
             for (int w = 0; w < 4; ++w) qop[tt][cc].w[w] = valid ? r.w[w] : 0u;
         }
     }
+    // tile bounds are the same in every lane: keep them in scalar registers so that
+    // the branches on them are scalar
     int p_wave_max = -1;
 #pragma unroll
-    for (int tt = 0; tt < TQ; ++tt) p_wave_max = max(p_wave_max, pt_max[tt]);
+    for (int tt = 0; tt < TQ; ++tt) {
+        pt_min[tt] = __builtin_amdgcn_readfirstlane(pt_min[tt]);
+        pt_max[tt] = __builtin_amdgcn_readfirstlane(pt_max[tt]);
+        p_wave_max = max(p_wave_max, pt_max[tt]);
+    }
 
     // ---- chunk loader: thread piece k is row (tid + k*NT) / PPR, 16-byte piece (tid % PPR)
     const char* kbase = reinterpret_cast<const char*>(a.k_pool);
@@ -121,11 +128,13 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
     const int pcolb = (tid % PPR) * 16;                  // byte offset in the row
     constexpr int RSTEP = NT / PPR;                      // rows between a thread's pieces
     int blk_next[PPT];                                   // block ids of the next chunk's rows
+    // loads are branch-free (indexes clamped into range, results masked) so that
+    // the compiler's wait counts stay exact
     auto load_table = [&](int ci) {
 #pragma unroll
         for (int k = 0; k < PPT; ++k) {
-            const int t = ci * kKT + prow + k * RSTEP;
-            blk_next[k] = t < kv_end ? trow[t >> a.log2_bs] : -1;
+            const int t = min(ci * kKT + prow + k * RSTEP, kv_end - 1);
+            blk_next[k] = trow[t >> a.log2_bs];
         }
     };
     Raw16 kraw[PPT], vraw[PPT];
@@ -135,11 +144,12 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
         for (int k = 0; k < PPT; ++k) {
             const int t = ci * kKT + prow + k * RSTEP;
             const int b = blk_next[k];
-            tlive[k] = t < kv_end && b >= 0 && b < a.num_blocks;
-            const int64_t row = tlive[k]
-                ? (((int64_t)b * a.num_kv_heads + g) << a.log2_bs) + (t & (bs - 1)) : 0;
-            kraw[k] = load16_stream(kbase + row * row_bytes + pcolb);
-            vraw[k] = load16_stream(vbase + row * row_bytes + pcolb);
+            tlive[k] = (t < kv_end) & (b >= 0) & (b < a.num_blocks);
+            const int bb = tlive[k] ? b : 0;            // absent: the pool's first row
+            const int64_t row =
+                ((int64_t)(bb * a.num_kv_heads + g) << a.log2_bs) + (tlive[k] ? (t & (bs - 1)) : 0);
+            kraw[k] = load16(kbase + row * row_bytes + pcolb);
+            vraw[k] = load16(vbase + row * row_bytes + pcolb);
         }
     };
     auto store_chunk = [&](int buf) {
@@ -183,78 +193,124 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
         const uint16_t* kt = ks[buf];
         const uint16_t* vt = vs[buf];
 #pragma unroll
-        for (int sub = 0; sub < kKT / 16; ++sub) {
-            const int u0 = t0 + 16 * sub;
-            if (u0 > p_wave_max) break;                  // uniform: nothing visible from here on
-            // K operands (A of the score MFMA): lane = token row, 8 head_dim numbers
-            Op8 kop[NC];
+        for (int sub = 0; sub < kKT / 32; ++sub) {
+            const int u0 = t0 + 32 * sub;
+            if (u0 > p_wave_max) break;                  // scalar: nothing visible from here on
+            // Two 16-token halves: K operands of each (A of the score MFMA: lane = token
+            // row, 8 head_dim numbers), presence flags of each, and per d-tile the V^T
+            // operand of the K=32 output MFMA, whose 8 numbers per lane are its 4 tokens
+            // of the first half then its 4 of the second (the order the score results
+            // of the two halves leave P^T in, so no data moves between lanes).
+            Op8 kop[2][NC];
 #pragma unroll
-            for (int cc = 0; cc < NC; ++cc) {
-                const uint4 r = *reinterpret_cast<const uint4*>(&kt[(16 * sub + c16) * LDK + 32 * cc + 8 * j]);
-                kop[cc].w[0] = r.x;
-                kop[cc].w[1] = r.y;
-                kop[cc].w[2] = r.z;
-                kop[cc].w[3] = r.w;
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int cc = 0; cc < NC; ++cc) {
+                    const uint4 r = *reinterpret_cast<const uint4*>(
+                        &kt[(32 * sub + 16 * h + c16) * LDK + 32 * cc + 8 * j]);
+                    kop[h][cc].w[0] = r.x;
+                    kop[h][cc].w[1] = r.y;
+                    kop[h][cc].w[2] = r.z;
+                    kop[h][cc].w[3] = r.w;
+                }
             }
-            const uint32_t lv4 = *reinterpret_cast<const uint32_t*>(&live_s[buf][16 * sub + 4 * j]);
-            Op4 pop[TQ], plo[TQ];
-            bool tile_on[TQ];
+            Op8 vop[NDT];
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const int rr = 32 * sub + 4 * j + (c16 >> 2);
+                const int cc = 16 * dt + 4 * (c16 & 3);
+                const Op4 v0 = read_tr16(&vt[rr * LDV + cc]);
+                const Op4 v1 = read_tr16(&vt[(rr + 16) * LDV + cc]);
+                vop[dt].w[0] = v0.w[0];
+                vop[dt].w[1] = v0.w[1];
+                vop[dt].w[2] = v1.w[0];
+                vop[dt].w[3] = v1.w[1];
+            }
+            uint32_t lv4[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                lv4[h] = *reinterpret_cast<const uint32_t*>(&live_s[buf][32 * sub + 16 * h + 4 * j]);
+            // scores of every tile first, so that no softmax waits on its own MFMAs
+            f32x4 sc[TQ][2];
 #pragma unroll
             for (int tt = 0; tt < TQ; ++tt) {
-                tile_on[tt] = u0 <= pt_max[tt];          // uniform
-                if (!tile_on[tt]) continue;
-                f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int cc = 0; cc < NC; ++cc) sc = mma32<DT>(kop[cc], qop[tt][cc], sc);
-                // causal mask only where the sub-chunk reaches past the tile's first position
-                const bool need_mask = u0 + 15 > pt_min[tt];
-                float sv[4];
-                bool live[4];
-                float mx = kNegInf;
+                for (int h = 0; h < 2; ++h) {
+                    sc[tt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = u0 + 4 * j + i;
-                    live[i] = ((lv4 >> (8 * i)) & 1u) && (!need_mask || t <= pcol[tt]);
-                    sv[i] = live[i] ? sc[i] * a.qk_scale : kNegInf;
-                    mx = fmaxf(mx, sv[i]);
+                    for (int cc = 0; cc < NC; ++cc) sc[tt][h] = mma32<DT>(kop[h][cc], qop[tt][cc], sc[tt][h]);
                 }
-                mx = max_over_groups(mx);
-                const float mn = (mx > m[tt] + kMaxSlack) ? mx : m[tt];
-                const bool moved = mn != m[tt];
-                const float alpha = moved ? fast_exp2(m[tt] - mn) : 1.0f;
-                float pr[4];
-                float psum = 0.0f;
+            }
+            // every token of the 32 present (a wavefront-uniform test)
+            const bool sub_full = __builtin_amdgcn_ballot_w64((lv4[0] & lv4[1]) != 0x01010101u) == 0;
+            Op8 pop[TQ], plo[TQ];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pr[i] = live[i] ? fast_exp2(sv[i] - mn) : 0.0f;
-                    psum += pr[i];
+            for (int tt = 0; tt < TQ; ++tt) {
+                // Token masks only where a token may be absent or the step reaches past
+                // the tile's first position (causal limit); scalar test, and the masked
+                // form is built without branches.  Value e = 4h + i is token u0+16h+4j+i.
+                float sv[8];
+                uint32_t live[8];
+                if (sub_full && u0 + 31 <= pt_min[tt]) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        live[e] = 1u;
+                        sv[e] = sc[tt][e >> 2][e & 3] * a.qk_scale;
+                    }
+                } else {
+                    const int lim = (u0 + 31 > pt_min[tt]) ? pcol[tt] : 0x7FFFFFFF;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int h = e >> 2, i = e & 3;
+                        const int t = u0 + 16 * h + 4 * j + i;
+                        live[e] = ((lv4[h] >> (8 * i)) & 1u) & (uint32_t)(t <= lim);
+                        sv[e] = live[e] ? sc[tt][h][i] * a.qk_scale : kNegInf;
+                    }
                 }
-                l[tt] = l[tt] * alpha + psum;
-                m[tt] = mn;
-                if (__builtin_amdgcn_ballot_w64(moved)) {
+                // The reference maximum moves only when a score passes it by more than
+                // kMaxSlack; a lane's own scores tell whether that can happen, and only
+                // then (rarely, after the first steps) is the column maximum taken across
+                // the four lanes of the column and the accumulators rescaled.
+                float lmax = sv[0];
+#pragma unroll
+                for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, sv[e]);
+                float mn = m[tt];
+                float alpha = 1.0f;
+                if (__builtin_amdgcn_ballot_w64(lmax > m[tt] + kMaxSlack)) {
+                    const float mx = max_over_groups(lmax);
+                    mn = (mx > m[tt] + kMaxSlack) ? mx : m[tt];
+                    const bool moved = mn != m[tt];
+                    alpha = moved ? fast_exp2(m[tt] - mn) : 1.0f;   // from -inf: 0
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] *= alpha;
+                    m[tt] = mn;
                 }
-                pop[tt].w[0] = pack2<DT>(pr[0], pr[1]);
-                pop[tt].w[1] = pack2<DT>(pr[2], pr[3]);
+                float pr[8];
+                float psum = 0.0f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    pr[e] = live[e] ? fast_exp2(sv[e] - mn) : 0.0f;
+                    psum += pr[e];
+                }
+                l[tt] = l[tt] * alpha + psum;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) pop[tt].w[q] = pack2<DT>(pr[2 * q], pr[2 * q + 1]);
                 if constexpr (DT == PA_BF16) {
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
+                    for (int q = 0; q < 4; ++q) {
                         const float h0 = __uint_as_float(pop[tt].w[q] << 16);
                         const float h1 = __uint_as_float(pop[tt].w[q] & 0xFFFF0000u);
                         plo[tt].w[q] = pack2<DT>(pr[2 * q] - h0, pr[2 * q + 1] - h1);
                     }
                 }
             }
-            // O^T[d][column] += V^T[d][token] · P^T[token][column], V^T read transposed
+            // O^T[d][column] += V^T[d][token] · P^T[token][column], 32 tokens per MFMA
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                const Op4 vop = read_tr16(&vt[(16 * sub + 4 * j + (c16 >> 2)) * LDV + 16 * dt + 4 * (c16 & 3)]);
 #pragma unroll
                 for (int tt = 0; tt < TQ; ++tt) {
-                    if (!tile_on[tt]) continue;
-                    acc[tt][dt] = mma16<DT>(vop, pop[tt], acc[tt][dt]);
-                    if constexpr (DT == PA_BF16) acc[tt][dt] = mma16<DT>(vop, plo[tt], acc[tt][dt]);
+                    acc[tt][dt] = mma32<DT>(vop[dt], pop[tt], acc[tt][dt]);
+                    if constexpr (DT == PA_BF16) acc[tt][dt] = mma32<DT>(vop[dt], plo[tt], acc[tt][dt]);
                 }
             }
         }
