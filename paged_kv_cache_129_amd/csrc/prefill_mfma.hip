@@ -15,8 +15,9 @@
 // matrix dimension.  A workgroup of NW wavefronts owns NW * TQ * 16 columns
 // (TQ 16-column tiles per wavefront) and streams the K/V tokens 0..p_last of
 // its last column in chunks of kKT tokens.  Each chunk is loaded once per
-// workgroup (16-byte global loads, one chunk ahead in registers, block ids
-// two chunks ahead) into double-buffered LDS tiles; every wavefront then runs
+// workgroup, one chunk ahead, by direct global-to-LDS 16-byte loads
+// (global_load_lds_dwordx4; block ids two chunks ahead) into double-buffered,
+// bank-swizzled LDS tiles; every wavefront then runs
 // on its own columns, 32 tokens at a time:
 //   * S^T[token][column] = K · Q^T on v_mfma_f32_16x16x32 (K from LDS as the
 //     A operand, row = token; the wavefront's queries stay in registers as B);
@@ -44,20 +45,21 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 
 template <int DT, int D, int NW, int TQ, int WPE>
 __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs a) {
-    constexpr int NC = D / 32;          // score MFMAs per sub-chunk and tile
+    constexpr int NC = D / 32;          // score MFMAs per step and tile
     constexpr int NDT = D / 16;         // output d-tiles
-    constexpr int LDK = D + 8;          // K tile row stride (halfs): 16 rows of a
-                                        // 16-byte column read hit distinct banks
-    constexpr int LDV = D + 16;         // V tile row stride (halfs): conflict-free
-                                        // transposed reads
-    constexpr int PPR = D * 2 / 16;     // 16-byte pieces per token row
-    constexpr int NT = NW * 64;
-    constexpr int PPT = kKT * PPR / NT; // pieces per thread per tensor and chunk
+    constexpr int ROWB = D * 2;         // bytes of one token row
+    constexpr int PPR = ROWB / 16;      // 16-byte pieces per row
+    constexpr int RPI = 64 / PPR;       // rows one wavefront load instruction fills
+    constexpr int NLI = kKT / (NW * RPI);   // load instructions per wavefront, tensor and chunk
     constexpr int CB = NW * TQ * 16;    // columns per workgroup
-    static_assert(PPT * NT == kKT * PPR, "chunk split");
+    static_assert(NLI * NW * RPI == kKT, "chunk split");
 
-    __shared__ __attribute__((aligned(16))) uint16_t ks[2][kKT * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[2][kKT * LDV];
+    // K and V chunks, double-buffered, rows of ROWB bytes with no padding: piece p
+    // of row r is stored at piece slot p ^ (r % PPR), so that the 16 rows of a
+    // K-operand read and the 4 rows of a transposed V read hit distinct banks.
+    // Chunks arrive by direct global-to-LDS loads (no registers in between).
+    __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][kKT * ROWB];
+    __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][kKT * ROWB];
     __shared__ __attribute__((aligned(4))) uint8_t live_s[2][kKT];
 
     const int tid = threadIdx.x;
@@ -120,49 +122,62 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
         p_wave_max = max(p_wave_max, pt_max[tt]);
     }
 
-    // ---- chunk loader: thread piece k is row (tid + k*NT) / PPR, 16-byte piece (tid % PPR)
+    // ---- chunk loader.  Load instruction k of wavefront w fills rows
+    // (w * NLI + k) * RPI .. + RPI - 1 of a chunk: lane i lands in piece slot i % PPR
+    // of row i / PPR (a direct load writes lane i's 16 bytes at base + 16 i), so it
+    // fetches the piece that belongs there, (i % PPR) ^ (row % PPR).
     const char* kbase = reinterpret_cast<const char*>(a.k_pool);
     const char* vbase = reinterpret_cast<const char*>(a.v_pool);
-    constexpr int64_t row_bytes = (int64_t)D * 2;
-    const int prow = tid / PPR;                          // first row of this thread
-    const int pcolb = (tid % PPR) * 16;                  // byte offset in the row
-    constexpr int RSTEP = NT / PPR;                      // rows between a thread's pieces
-    int blk_next[PPT];                                   // block ids of the next chunk's rows
-    // loads are branch-free (indexes clamped into range, results masked) so that
-    // the compiler's wait counts stay exact
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const int lslot = lane % PPR;
+    int lrow[NLI];
+    uint32_t lpiece[NLI];
+#pragma unroll
+    for (int k = 0; k < NLI; ++k) {
+        lrow[k] = (wu * NLI + k) * RPI + lane / PPR;
+        lpiece[k] = (uint32_t)(lslot ^ (lrow[k] % PPR)) * 16u;
+    }
+    int blk_next[NLI];                   // block ids of the rows of the next chunk to load
+    // table loads are branch-free (index clamped into range) so that the compiler's
+    // wait counts stay exact
     auto load_table = [&](int ci) {
 #pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const int t = min(ci * kKT + prow + k * RSTEP, kv_end - 1);
+        for (int k = 0; k < NLI; ++k) {
+            const int t = min(ci * kKT + lrow[k], kv_end - 1);
             blk_next[k] = trow[t >> a.log2_bs];
         }
     };
-    Raw16 kraw[PPT], vraw[PPT];
-    bool tlive[PPT];
-    auto load_data = [&](int ci) {
+    uint32_t absent_rows = 0;            // bit k: row of instruction k holds no token
+    auto issue_chunk = [&](int ci, int buf) {
+        absent_rows = 0;
 #pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const int t = ci * kKT + prow + k * RSTEP;
+        for (int k = 0; k < NLI; ++k) {
+            const int t = ci * kKT + lrow[k];
             const int b = blk_next[k];
-            tlive[k] = (t < kv_end) & (b >= 0) & (b < a.num_blocks);
-            const int bb = tlive[k] ? b : 0;            // absent: the pool's first row
-            const int64_t row =
-                ((int64_t)(bb * a.num_kv_heads + g) << a.log2_bs) + (tlive[k] ? (t & (bs - 1)) : 0);
-            kraw[k] = load16(kbase + row * row_bytes + pcolb);
-            vraw[k] = load16(vbase + row * row_bytes + pcolb);
+            const bool live = (t < kv_end) & (b >= 0) & (b < a.num_blocks);
+            const int bb = live ? b : 0;            // absent: the pool's first row
+            const int64_t off =
+                (((int64_t)(bb * a.num_kv_heads + g) << a.log2_bs) + (live ? (t & (bs - 1)) : 0)) * ROWB +
+                lpiece[k];
+            const int lbase = (wu * NLI + k) * RPI * ROWB;
+            __builtin_amdgcn_global_load_lds(kbase + off, (__attribute__((address_space(3))) void*)&kbuf[buf][lbase],
+                                             16, 0, 0);
+            __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)&vbuf[buf][lbase],
+                                             16, 0, 0);
+            absent_rows |= live ? 0u : (1u << k);
+            if (lslot == 0) live_s[buf][lrow[k]] = live ? 1 : 0;
         }
     };
-    auto store_chunk = [&](int buf) {
+    // after this wavefront's loads of a chunk have landed: zero the V rows that hold
+    // no token (their weights are zero, and 0 * NaN would poison the sums)
+    auto settle_chunk = [&](int buf) {
+        __builtin_amdgcn_s_waitcnt(0);           // vmcnt(0): the direct loads are in LDS
+        if (absent_rows) {
 #pragma unroll
-        for (int k = 0; k < PPT; ++k) {
-            const int r = prow + k * RSTEP;
-            uint16_t* kd = &ks[buf][r * LDK + pcolb / 2];
-            uint16_t* vd = &vs[buf][r * LDV + pcolb / 2];
-            *reinterpret_cast<uint4*>(kd) = make_uint4(kraw[k].w[0], kraw[k].w[1], kraw[k].w[2], kraw[k].w[3]);
-            const bool lv = tlive[k];
-            *reinterpret_cast<uint4*>(vd) = lv ? make_uint4(vraw[k].w[0], vraw[k].w[1], vraw[k].w[2], vraw[k].w[3])
-                                               : make_uint4(0u, 0u, 0u, 0u);
-            if (pcolb == 0) live_s[buf][r] = lv ? 1 : 0;
+            for (int k = 0; k < NLI; ++k)
+                if (absent_rows & (1u << k))
+                    *reinterpret_cast<uint4*>(&vbuf[buf][(wu * NLI + k) * RPI * ROWB + lane * 16]) =
+                        make_uint4(0u, 0u, 0u, 0u);
         }
     };
 
@@ -178,124 +193,93 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
 
     if (nchunks > 0) {
         load_table(0);
-        load_data(0);
+        issue_chunk(0, 0);
         if (nchunks > 1) load_table(1);
     }
     for (int ci = 0; ci < nchunks; ++ci) {
         const int buf = ci & 1;
-        store_chunk(buf);
+        settle_chunk(buf);
         __syncthreads();
         if (ci + 1 < nchunks) {
-            load_data(ci + 1);
+            issue_chunk(ci + 1, buf ^ 1);
             if (ci + 2 < nchunks) load_table(ci + 2);
         }
         const int t0 = ci * kKT;
-        const uint16_t* kt = ks[buf];
-        const uint16_t* vt = vs[buf];
-#pragma unroll
-        for (int sub = 0; sub < kKT / 32; ++sub) {
-            const int u0 = t0 + 32 * sub;
-            if (u0 > p_wave_max) break;                  // scalar: nothing visible from here on
-            // Two 16-token halves: K operands of each (A of the score MFMA: lane = token
-            // row, 8 head_dim numbers), presence flags of each, and per d-tile the V^T
-            // operand of the K=32 output MFMA, whose 8 numbers per lane are its 4 tokens
-            // of the first half then its 4 of the second (the order the score results
-            // of the two halves leave P^T in, so no data moves between lanes).
-            Op8 kop[2][NC];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-#pragma unroll
-                for (int cc = 0; cc < NC; ++cc) {
-                    const uint4 r = *reinterpret_cast<const uint4*>(
-                        &kt[(32 * sub + 16 * h + c16) * LDK + 32 * cc + 8 * j]);
-                    kop[h][cc].w[0] = r.x;
-                    kop[h][cc].w[1] = r.y;
-                    kop[h][cc].w[2] = r.z;
-                    kop[h][cc].w[3] = r.w;
-                }
-            }
-            Op8 vop[NDT];
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
-                const int rr = 32 * sub + 4 * j + (c16 >> 2);
-                const int cc = 16 * dt + 4 * (c16 & 3);
-                const Op4 v0 = read_tr16(&vt[rr * LDV + cc]);
-                const Op4 v1 = read_tr16(&vt[(rr + 16) * LDV + cc]);
-                vop[dt].w[0] = v0.w[0];
-                vop[dt].w[1] = v0.w[1];
-                vop[dt].w[2] = v1.w[0];
-                vop[dt].w[3] = v1.w[1];
-            }
-            uint32_t lv4[2];
+        const uint8_t* kt = kbuf[buf];
+        const uint8_t* vt = vbuf[buf];
+        // Two 32-token steps per chunk.  The score MFMAs of both are issued first, so
+        // that the matrix cores work on the second step's scores while the vector
+        // units run the first step's softmax, and on the first step's output MFMAs
+        // while they run the second's.
+        const bool on0 = t0 <= p_wave_max, on1 = t0 + 32 <= p_wave_max;   // scalar
+        f32x4 scs[2][TQ][2];
+        uint32_t lvs[2][2];
+        auto scores = [&](int sub) {
+            uint32_t* lv4 = lvs[sub];
+            auto& sc = scs[sub];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 lv4[h] = *reinterpret_cast<const uint32_t*>(&live_s[buf][32 * sub + 16 * h + 4 * j]);
-            // scores of every tile first, so that no softmax waits on its own MFMAs
-            f32x4 sc[TQ][2];
+            // scores of every tile first, so that no softmax waits on its own MFMAs; each
+            // K operand is read just before the MFMAs that use it (few registers live)
 #pragma unroll
             for (int tt = 0; tt < TQ; ++tt) {
+                sc[tt][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                sc[tt][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    sc[tt][h] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int h = 0; h < 2; ++h) {
+                const int row = 32 * sub + 16 * h + c16;
 #pragma unroll
-                    for (int cc = 0; cc < NC; ++cc) sc[tt][h] = mma32<DT>(kop[h][cc], qop[tt][cc], sc[tt][h]);
+                for (int cc = 0; cc < NC; ++cc) {
+                    const uint4 r = *reinterpret_cast<const uint4*>(
+                        &kt[row * ROWB + (((4 * cc + j) ^ (row % PPR)) * 16)]);
+                    const Op8 kop{{r.x, r.y, r.z, r.w}};
+#pragma unroll
+                    for (int tt = 0; tt < TQ; ++tt) sc[tt][h] = mma32<DT>(kop, qop[tt][cc], sc[tt][h]);
                 }
             }
+        };
+        auto step = [&](int sub) {
+            const int u0 = t0 + 32 * sub;
+            const uint32_t* lv4 = lvs[sub];
+            auto& sc = scs[sub];
             // every token of the 32 present (a wavefront-uniform test)
             const bool sub_full = __builtin_amdgcn_ballot_w64((lv4[0] & lv4[1]) != 0x01010101u) == 0;
             Op8 pop[TQ], plo[TQ];
-#pragma unroll
-            for (int tt = 0; tt < TQ; ++tt) {
-                // Token masks only where a token may be absent or the step reaches past
-                // the tile's first position (causal limit); scalar test, and the masked
-                // form is built without branches.  Value e = 4h + i is token u0+16h+4j+i.
-                float sv[8];
-                uint32_t live[8];
-                if (sub_full && u0 + 31 <= pt_min[tt]) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        live[e] = 1u;
-                        sv[e] = sc[tt][e >> 2][e & 3] * a.qk_scale;
-                    }
-                } else {
-                    const int lim = (u0 + 31 > pt_min[tt]) ? pcol[tt] : 0x7FFFFFFF;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int h = e >> 2, i = e & 3;
-                        const int t = u0 + 16 * h + 4 * j + i;
-                        live[e] = ((lv4[h] >> (8 * i)) & 1u) & (uint32_t)(t <= lim);
-                        sv[e] = live[e] ? sc[tt][h][i] * a.qk_scale : kNegInf;
-                    }
-                }
-                // The reference maximum moves only when a score passes it by more than
-                // kMaxSlack; a lane's own scores tell whether that can happen, and only
-                // then (rarely, after the first steps) is the column maximum taken across
-                // the four lanes of the column and the accumulators rescaled.
-                float lmax = sv[0];
-#pragma unroll
-                for (int e = 1; e < 8; ++e) lmax = fmaxf(lmax, sv[e]);
-                float mn = m[tt];
-                float alpha = 1.0f;
+            // The reference maximum moves only when a score passes it by more than
+            // kMaxSlack; a lane's own scores tell whether that can happen, and only
+            // then (rarely, after the first steps) is the column maximum taken across
+            // the four lanes of the column.  Returns whether it moved (wavefront-uniform);
+            // the accumulators are rescaled once, after the masked and unmasked paths
+            // have joined, so that the paths share their registers.
+            auto update_max = [&](int tt, float lmax, float& alpha) -> bool {
                 if (__builtin_amdgcn_ballot_w64(lmax > m[tt] + kMaxSlack)) {
                     const float mx = max_over_groups(lmax);
-                    mn = (mx > m[tt] + kMaxSlack) ? mx : m[tt];
-                    const bool moved = mn != m[tt];
-                    alpha = moved ? fast_exp2(m[tt] - mn) : 1.0f;   // from -inf: 0
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] *= alpha;
+                    const float mn = (mx > m[tt] + kMaxSlack) ? mx : m[tt];
+                    alpha = mn != m[tt] ? fast_exp2(m[tt] - mn) : 1.0f;   // from -inf: 0
                     m[tt] = mn;
+                    return true;
                 }
-                float pr[8];
-                float psum = 0.0f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pr[e] = live[e] ? fast_exp2(sv[e] - mn) : 0.0f;
-                    psum += pr[e];
-                }
-                l[tt] = l[tt] * alpha + psum;
+                return false;
+            };
+            // weights -> MFMA operands; the running sum adds the weights as the MFMA
+            // sees them (fp16: the rounded values, two per dot instruction)
+            auto finish = [&](int tt, const float* pr) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) pop[tt].w[q] = pack2<DT>(pr[2 * q], pr[2 * q + 1]);
-                if constexpr (DT == PA_BF16) {
+                if constexpr (DT == PA_F16) {
+                    float lt = l[tt];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        lt = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pop[tt].w[q]),
+                                                    half2_t{(_Float16)1.0f, (_Float16)1.0f}, lt, false);
+                    l[tt] = lt;
+                } else {
+                    float psum = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) psum += pr[e];
+                    l[tt] += psum;
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const float h0 = __uint_as_float(pop[tt].w[q] << 16);
@@ -303,17 +287,79 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
                         plo[tt].w[q] = pack2<DT>(pr[2 * q] - h0, pr[2 * q + 1] - h1);
                     }
                 }
+            };
+            const bool pos_scale = a.qk_scale > 0.0f;
+#pragma unroll
+            for (int tt = 0; tt < TQ; ++tt) {
+                // value e = 4h + i is token u0 + 16h + 4j + i
+                float pr[8];
+                float alpha = 1.0f;
+                bool rescale;
+                if (sub_full && u0 + 31 <= pt_min[tt] && pos_scale) {
+                    // every token present and visible: no masks; with a positive scale
+                    // the largest scaled score is the scaled largest score
+                    float smax = sc[tt][0][0];
+#pragma unroll
+                    for (int e = 1; e < 8; ++e) smax = fmaxf(smax, sc[tt][e >> 2][e & 3]);
+                    rescale = update_max(tt, smax * a.qk_scale, alpha);
+                    const float mn = m[tt];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(fmaf(sc[tt][e >> 2][e & 3], a.qk_scale, -mn));
+                } else {
+                    // absent tokens and the causal limit, masked without branches
+                    const int lim = (u0 + 31 > pt_min[tt]) ? pcol[tt] : 0x7FFFFFFF;
+                    float sv[8];
+                    uint32_t live[8];
+                    float lmax = kNegInf;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int h = e >> 2, i = e & 3;
+                        const int t = u0 + 16 * h + 4 * j + i;
+                        live[e] = ((lv4[h] >> (8 * i)) & 1u) & (uint32_t)(t <= lim);
+                        sv[e] = live[e] ? sc[tt][h][i] * a.qk_scale : kNegInf;
+                        lmax = fmaxf(lmax, sv[e]);
+                    }
+                    rescale = update_max(tt, lmax, alpha);
+                    const float mn = m[tt];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) pr[e] = live[e] ? fast_exp2(sv[e] - mn) : 0.0f;
+                }
+                if (rescale) {                              // wavefront-uniform, rare
+#pragma unroll
+                    for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] *= alpha;
+                    l[tt] *= alpha;
+                }
+                finish(tt, pr);
             }
             // O^T[d][column] += V^T[d][token] · P^T[token][column], 32 tokens per MFMA
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
+                // V^T operand of d-tile dt: row rr, halfs 16 dt + 4 (c16 & 3) .. + 3, i.e.
+                // piece 2 dt + (c16 & 3) / 2, its first or second 8 bytes
+                Op8 vop;
+                {
+                    const int rr = 32 * sub + 4 * j + (c16 >> 2);
+                    const int pc = 2 * dt + ((c16 & 3) >> 1), hb = (c16 & 1) * 8;
+                    const Op4 v0 = read_tr16(reinterpret_cast<const uint16_t*>(
+                        &vt[rr * ROWB + ((pc ^ (rr % PPR)) * 16) + hb]));
+                    const Op4 v1 = read_tr16(reinterpret_cast<const uint16_t*>(
+                        &vt[(rr + 16) * ROWB + ((pc ^ ((rr + 16) % PPR)) * 16) + hb]));
+                    vop.w[0] = v0.w[0];
+                    vop.w[1] = v0.w[1];
+                    vop.w[2] = v1.w[0];
+                    vop.w[3] = v1.w[1];
+                }
 #pragma unroll
                 for (int tt = 0; tt < TQ; ++tt) {
-                    acc[tt][dt] = mma32<DT>(vop[dt], pop[tt], acc[tt][dt]);
-                    if constexpr (DT == PA_BF16) acc[tt][dt] = mma32<DT>(vop[dt], plo[tt], acc[tt][dt]);
+                    acc[tt][dt] = mma32<DT>(vop, pop[tt], acc[tt][dt]);
+                    if constexpr (DT == PA_BF16) acc[tt][dt] = mma32<DT>(vop, plo[tt], acc[tt][dt]);
                 }
             }
-        }
+        };
+        if (on0) scores(0);
+        if (on1) scores(1);
+        if (on0) step(0);
+        if (on1) step(1);
         // no barrier here: the next chunk goes into the other buffer, and the
         // barrier after that store orders this chunk's reads before the buffer
         // is written again
