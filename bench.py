@@ -96,6 +96,13 @@ class Workload:
                 "block_size": self.bs, "kv_dtype": self.kv_dtype, "q_dtype": self.q_dtype,
                 "context_lens": self.ctx_desc, "partition_size": self.partition_size}
 
+    def roofline(self, call_ms):
+        """Decode is bound by HBM: algorithmic bytes per call over the call time."""
+        achieved = self.attn_bytes / (call_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                "algorithmic_bytes_per_launch": self.attn_bytes}
+
     def cpu_inputs(self, l, s):
         """Host copies of what the oracle needs for sequence s of layer l: the
         sequence's blocks (a local table 0..n-1), its new K/V and its query."""
@@ -319,12 +326,137 @@ class Tiny(HostLayers):
         self.finish(pa, torch, partition_size, self.ctx.max())
 
 
+PEAK_MFMA_F16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 matrix-core peak
+
+
+class Llama7BPrefill(Workload):
+    """Llama-2-7B-shaped chunked prefill over 32 layers: 8 sequences with 0, 512, ...,
+    3,584 tokens cached and a 512-token chunk each (contexts 512..4096), 32 heads x
+    128, fp16, block 16.  A step writes the chunk's K/V and runs causal multi-token
+    attention in every layer (layers are copies of layer 0 in their own memory).
+    Bound by the matrix cores: flops = 4 x (visible query-key pairs) x heads x head_dim."""
+    name = "llama2-7b chunked prefill step, 32 layers, fp16 KV, 512-token chunks"
+    bound = "mfma"
+
+    def __init__(self, pa, W, torch, partition_size, args):
+        case = W.llama7b_prefill_case()
+        self.case = case
+        self.pa, self.torch = pa, torch
+        self.S, self.H, self.Hkv, self.D = case.num_seqs, case.num_heads, case.num_kv_heads, case.head_dim
+        self.bs, self.NB, self.L = case.block_size, case.num_blocks, args.layers or 32
+        self.kv_dtype, self.q_dtype = case.kv_dtype, case.q_dtype
+        self.scale = case.scale
+        self.ctx = case.context_lens.astype(np.int32)
+        self.partition_size = 0
+        base = upload_case(case, torch)
+        self.layers = [base] + [{k: v.clone() for k, v in base.items()} for _ in range(self.L - 1)]
+        for d in self.layers:
+            d["out"] = torch.empty_like(d["q"])
+        self.tables = torch.from_numpy(case.block_tables.astype(np.int32)).cuda()
+        self.ctx_t = torch.from_numpy(self.ctx).cuda()
+        self.qs = torch.from_numpy(case.query_start.astype(np.int32)).cuda()
+        self.slots = torch.from_numpy(case.slot_mapping.astype(np.int64)).cuda()
+        T = case.num_tokens
+        pairs = 0
+        for s in range(self.S):
+            n, ql = int(self.ctx[s]), int(case.query_start[s + 1] - case.query_start[s])
+            pairs += ql * (n - ql) + ql * (ql + 1) // 2
+        self.pairs = None
+        self.visible_pairs = pairs
+        self.flops = 4 * pairs * self.H * self.D
+        self.attn_bytes = int(self.ctx.sum()) * 2 * self.Hkv * self.D * 2 + 2 * T * self.H * self.D * 2
+        self.write_bytes = write_bytes(T, self.Hkv, self.D, 2, 2)
+        self.step_bytes = self.L * (self.attn_bytes + self.write_bytes)
+        self.seq_layers_per_step = T * self.L          # query tokens x layers
+        torch.cuda.synchronize()
+
+    def decode(self, l):
+        d = self.layers[l]
+        self.pa.paged_attention_prefill(d["out"], d["q"], d["k_pool"], d["v_pool"], self.tables,
+                                        self.ctx_t, self.qs, max_query_len=self.case.max_query_len,
+                                        scale=self.scale)
+
+    def step(self):
+        for l in range(self.L):
+            d = self.layers[l]
+            self.pa.kv_cache_write(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], self.slots)
+            self.decode(l)
+
+    def roofline(self, call_ms):
+        achieved = self.flops / (call_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_MFMA_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_MFMA_F16_TFLOPS, 4),
+                "flops_per_launch": self.flops}
+
+    def config(self):
+        return {"workload": self.name, "num_seqs": self.S, "num_layers": self.L,
+                "num_heads": self.H, "num_kv_heads": self.Hkv, "head_dim": self.D,
+                "block_size": self.bs, "kv_dtype": self.kv_dtype, "q_dtype": self.q_dtype,
+                "cached_tokens": [int(x) for x in self.ctx - 512], "chunk_tokens": 512,
+                "visible_query_key_pairs": self.visible_pairs}
+
+    def cpu_inputs(self, l, s):
+        """Host copies for 8 query rows of sequence s of layer l spread over its chunk
+        (the oracle computes only those rows)."""
+        torch = self.torch
+        d = self.layers[l]
+        case = self.case
+        n = int(self.ctx[s])
+        nblk = (n + self.bs - 1) // self.bs
+        idx = torch.from_numpy(case.block_tables[s, :nblk].astype(np.int64)).cuda()
+        r0, r1 = int(case.query_start[s]), int(case.query_start[s + 1])
+        rows = np.linspace(0, r1 - r0 - 1, 8).astype(int)
+        return dict(kp=raw_np(d["k_pool"][idx]), vp=raw_np(d["v_pool"][idx]),
+                    kn=raw_np(d["k_new"][r0:r1]), vn=raw_np(d["v_new"][r0:r1]),
+                    q=raw_np(d["q"][r0:r1]), n=n, ql=r1 - r0, rows=rows,
+                    slot=self._local_slots(s, nblk),
+                    local=np.arange(nblk, dtype=np.int32)[None, :])
+
+    def _local_slots(self, s, nblk):
+        """The chunk's slots renumbered for the copied blocks (local table 0..nblk-1)."""
+        case = self.case
+        r0, r1 = int(case.query_start[s]), int(case.query_start[s + 1])
+        phys = case.block_tables[s, :nblk]
+        where = {int(b): i for i, b in enumerate(phys)}
+        sl = case.slot_mapping[r0:r1]
+        return np.array([where[int(x) // self.bs] * self.bs + int(x) % self.bs for x in sl], np.int64)
+
+    def cpu_run(self, oracle, x):
+        oracle.kv_write(x["kp"], x["vp"], self.kv_dtype, x["kn"], x["vn"], self.q_dtype, x["slot"],
+                        self.bs)
+        oracle.paged_prefill(x["q"], self.q_dtype, x["kp"], x["vp"], self.kv_dtype, x["local"],
+                             [x["n"]], [0, x["ql"]], self.bs, self.scale, rows=x["rows"])
+
+    def cpu_sample(self, oracle, budget_s, cores):
+        """Oracle throughput in query rows per second: 8 rows of each sequence-layer
+        (spread over its chunk, so over the whole range of visible lengths), longest
+        contexts first, `cores` sequence-layers at a time on a thread pool."""
+        import concurrent.futures as cf
+        order = np.argsort(-self.ctx, kind="stable")
+        work = [(l, int(s)) for l in range(self.L) for s in order]
+        rows, secs, i = 0, 0.0, 0
+        with cf.ThreadPoolExecutor(cores) as ex:
+            while i < len(work) and secs < budget_s:
+                batch = work[i:i + cores]
+                i += len(batch)
+                xs = [self.cpu_inputs(l, s) for l, s in batch]
+                t0 = time.perf_counter()
+                list(ex.map(lambda x: self.cpu_run(oracle, x), xs))
+                secs += time.perf_counter() - t0
+                rows += 8 * len(batch)
+        return {"value": round(rows / secs, 3), "unit": "query-token-layers/s", "cores": cores,
+                "kind": "oracle", "sample": f"{rows} query rows (8 per sequence-layer, spread over "
+                f"each chunk), longest contexts first, {cores} sequence-layers at a time",
+                "cpu_model": cpu_model(), "host_cpus": os.cpu_count(), "seconds": round(secs, 2)}
+
+
 # launch configuration per workload: the fastest measured on MI355X (uniform
 # long contexts: one pass per (sequence, head); ragged batches: balanced split)
-DEFAULT_PARTITION = {"llama7b": 0, "opt13b": -1, "falcon7b": -1, "llama70b": -1, "tiny": 0}
+DEFAULT_PARTITION = {"llama7b": 0, "opt13b": -1, "falcon7b": -1, "llama70b": -1, "tiny": 0,
+                     "llama7b_prefill": 0}
 
 WORKLOADS = {"llama7b": Llama7B, "opt13b": Opt13B, "falcon7b": Falcon7B, "llama70b": Llama70B,
-             "tiny": Tiny}
+             "tiny": Tiny, "llama7b_prefill": Llama7BPrefill}
 
 
 def read_traffic(workload, partition_size, block_size):
@@ -448,31 +580,31 @@ def config_entry(key, wl, torch, oracle, args, cpu_seconds, cores):
     """Measurements of one workload for the per-config list of the bench line."""
     ms, dec_ms, spread = measure(wl, torch, args.steps, args.warmup, args.decode_iters,
                                  graph=not args.no_graph)
-    achieved = wl.attn_bytes / (dec_ms * 1e-3) / 1e9
+    roof = wl.roofline(dec_ms)
     traffic, src = read_traffic(key, wl.partition_size, wl.bs)
+    att = {"avg_launch_us": round(dec_ms * 1e3, 2), **roof,
+           "single_call_us_p10_p50_p90": spread, "traffic": traffic,
+           "traffic_ratio": None if traffic is None else round(traffic / wl.attn_bytes, 4),
+           "traffic_source": src}
+    if hasattr(wl, "logical_attn_bytes"):
+        att["logical_bytes_per_launch"] = wl.logical_attn_bytes
     e = {"workload": key, "config": wl.config(), "ms_per_step": round(ms, 4),
          "step_gbs": round(wl.step_bytes / (ms * 1e-3) / 1e9, 1),
-         "decode_tokens_per_s": round(wl.seq_layers_per_step / (ms * 1e-3), 1),
-         "attention": {"avg_launch_us": round(dec_ms * 1e3, 2), "achieved_gbs": round(achieved, 1),
-                       "frac": round(achieved / PEAK_HBM_GBS, 4),
-                       "algorithmic_bytes_per_launch": wl.attn_bytes,
-                       "single_call_us_p10_p50_p90": spread, "traffic": traffic,
-                       "traffic_ratio": None if traffic is None else round(traffic / wl.attn_bytes, 4),
-                       "traffic_source": src}}
-    if hasattr(wl, "logical_attn_bytes"):
-        e["attention"]["logical_bytes_per_launch"] = wl.logical_attn_bytes
+         "tokens_per_s": round(wl.seq_layers_per_step / (ms * 1e-3), 1),
+         "tokens": "query tokens x layers" if roof["bound"] == "mfma" else "sequences x layers",
+         "attention": att}
     log(f"[{key} bs{wl.bs}] {ms:.3f} ms/step, attention {dec_ms * 1e3:.1f} us "
-        f"({achieved:.0f} GB/s, {achieved / PEAK_HBM_GBS:.3f} of peak)")
+        f"({roof['achieved']} {roof['unit']}, {roof['frac']:.3f} of peak)")
     if cpu_seconds > 0:
         e["cpu_baseline"] = wl.cpu_sample(oracle, cpu_seconds, cores)
-        log(f"[{key}] cpu oracle: {e['cpu_baseline']['value']} seq-layers/s on {cores} threads")
+        log(f"[{key}] cpu oracle: {e['cpu_baseline']['value']} {e['cpu_baseline']['unit']} on {cores} threads")
     return e
 
 
 # every configuration of the workload set, measured after the headline one
 CONFIG_SET = [("tiny", {}), ("opt13b", {}), ("llama70b", {}), ("falcon7b", {"block_size": 8}),
               ("falcon7b", {"block_size": 16}), ("falcon7b", {"block_size": 32}),
-              ("falcon7b", {"block_size": 64})]
+              ("falcon7b", {"block_size": 64}), ("llama7b_prefill", {})]
 
 
 def main():
@@ -522,8 +654,8 @@ def main():
     ms_per_step, decode_ms, spread = measure(wl, torch, args.steps, args.warmup,
                                              args.decode_iters, graph=not args.no_graph)
     log(f"timed {args.steps} steps: {ms_per_step:.3f} ms/step")
-    achieved = wl.attn_bytes / (decode_ms * 1e-3) / 1e9
-    log(f"decode attention: {decode_ms * 1e3:.1f} us per launch, {achieved:.0f} GB/s")
+    roof = wl.roofline(decode_ms)
+    log(f"attention: {decode_ms * 1e3:.1f} us per launch, {roof['achieved']} {roof['unit']}")
     log(f"single calls: p10 {spread[0]} p50 {spread[1]} p90 {spread[2]} us")
 
     value = wl.step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -544,12 +676,11 @@ def main():
         "config": wl.config(),
         "pct_of_hbm_peak": round(100.0 * value / PEAK_HBM_GBS, 2),
         "decode_tokens_per_s": round(wl.seq_layers_per_step / (ms_per_step * 1e-3), 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "paged_attention_decode",
+        "roofline": {**roof, "traffic": traffic,
+                     "kernel": "paged_attention_prefill" if roof["bound"] == "mfma"
+                     else "paged_attention_decode",
                      "avg_launch_us": round(decode_ms * 1e3, 2),
                      "single_call_us_p10_p50_p90": spread,
-                     "algorithmic_bytes_per_launch": wl.attn_bytes,
                      "traffic_source": traffic_src,
                      "reference_copy_gbs": round(copy_gbs, 1)},
         "cpu_baseline": None,
@@ -558,7 +689,7 @@ def main():
     cores = cpu_cores()
     if args.cpu_seconds > 0:
         line["cpu_baseline"] = wl.cpu_sample(oracle, args.cpu_seconds, cores)
-        log(f"cpu oracle: {line['cpu_baseline']['value']} seq-layers/s on {cores} threads")
+        log(f"cpu oracle: {line['cpu_baseline']['value']} {line['cpu_baseline']['unit']} on {cores} threads")
 
     if not args.no_configs:
         del wl
