@@ -501,6 +501,139 @@ def calibrate_copy(pa, torch, mib):
     log(f"calibration copy: {mib} MiB read + {mib} MiB written per pool, K and V pools")
 
 
+# ---------------------------------------------------------------- allocator study (host only)
+class ReserveAhead:
+    """A contiguous-reservation policy of the kind paging replaces (KV 缓存与分页注意力
+    §04-§05): every admitted request reserves one contiguous run of token slots up
+    front, placed first-fit in a linear slot space (so gaps between runs are the
+    external fragments); `reserve(final_len)` gives the run length."""
+
+    def __init__(self, capacity, reserve):
+        self.capacity, self.reserve = capacity, reserve
+        self.runs = {}                     # request -> (start, length)
+
+    def admit(self, rid, first_len, final_len):
+        size = self.reserve(final_len)
+        pos = 0
+        for start, length in sorted(self.runs.values()):
+            if start - pos >= size:
+                break
+            pos = max(pos, start + length)
+        if pos + size > self.capacity:
+            return False
+        self.runs[rid] = (pos, size)
+        return True
+
+    def grow_all(self, rids):              # each run already holds its whole request
+        return True
+
+    def free(self, rid):
+        del self.runs[rid]
+
+    def reserved(self):
+        return sum(length for _, length in self.runs.values())
+
+
+class Paged:
+    """The library's block allocator: blocks taken as tokens arrive (§06-§07)."""
+
+    def __init__(self, pa, capacity, block_size):
+        self.a = pa.BlockAllocator(capacity // block_size, block_size)
+        self.bs, self.pa = block_size, pa
+
+    def admit(self, rid, first_len, final_len):
+        try:
+            self.a.add_seq(rid, first_len)
+            return True
+        except self.pa.PagedAttnError:
+            return False
+
+    def grow_all(self, rids):              # one slot for each, all or none
+        if not rids:
+            return True
+        try:
+            self.a.append_slots(rids)
+            return True
+        except self.pa.PagedAttnError:
+            return False
+
+    def free(self, rid):
+        self.a.free_seq(rid)
+
+    def reserved(self):
+        return self.a.stats()["used_blocks"] * self.bs
+
+
+def serve_trace(policy, prompts, finals, max_rounds=200000):
+    """Requests queued first come first served; each round admits from the head of
+    the queue while the policy finds room (a request's prompt lands at once; no
+    admission in a round that followed a preemption), then every running request
+    writes one token; when that needs room the policy cannot find, the latest
+    admitted request gives way (all of its memory: §09) and goes back to the head
+    of the queue to start again, until the rest fit.  Readouts: memory holding
+    tokens over memory reserved (mean over rounds), concurrent requests (max and
+    mean), rounds to finish."""
+    queue = list(range(len(prompts)))
+    running, written = [], {}
+    util, conc, rounds = [], [], 0
+    preempted = False
+    while (queue or running) and rounds < max_rounds:
+        rounds += 1
+        while queue and not preempted and policy.admit(queue[0], prompts[queue[0]], finals[queue[0]]):
+            rid = queue.pop(0)
+            running.append(rid)
+            written[rid] = prompts[rid]
+        preempted = False
+        while True:
+            growing = [r for r in running if written[r] < finals[r]]
+            if policy.grow_all(growing):
+                break
+            late = running.pop()                       # latest admitted gives way
+            policy.free(late)
+            queue.insert(0, late)
+            preempted = True
+        for r in running:
+            written[r] = min(finals[r], written[r] + 1)
+        conc.append(len(running))
+        res = policy.reserved()
+        util.append(sum(written[r] for r in running) / res if res else 1.0)
+        done = [r for r in running if written[r] >= finals[r]]
+        for rid in done:
+            policy.free(rid)
+        running = [r for r in running if written[r] < finals[r]]
+    return {"utilisation": round(float(np.mean(util)), 4), "max_concurrent": int(max(conc)),
+            "mean_concurrent": round(float(np.mean(conc)), 2), "rounds": rounds}
+
+
+def allocator_study(pa):
+    """Utilisation of KV memory by block size and by reservation policy, on seeded
+    synthetic traces (host only, the library's allocator for the paged policies).
+
+    * The pages' toy machine (KV 缓存与分页注意力 §14): 176 token slots, 40
+      requests of 1..20 tokens (uniform), one token per round; blocks of 1, 2, 4,
+      8 or 16 tokens against reserving 20 slots per request.
+    * An OPT-13B-sized cache (§03: 12 GB, about 15,700 tokens) serving 400
+      requests of log-normal prompt (median 160) and output (median 240) lengths,
+      at most 2,048 tokens: blocks of 16 against reserving the maximum, the next
+      power of two of the final length, or exactly the final length (the three
+      reservation policies of §05)."""
+    rng = np.random.default_rng(20230914)
+    toy_final = rng.integers(1, 21, size=40)
+    toy = {f"block_{bs}": serve_trace(Paged(pa, 176, bs), [1] * 40, toy_final.tolist())
+           for bs in (1, 2, 4, 8, 16)}
+    toy["reserve_20"] = serve_trace(ReserveAhead(176, lambda f: 20), [1] * 40, toy_final.tolist())
+    cap, max_len = 15700, 2048
+    prompt = np.clip(np.rint(rng.lognormal(np.log(160), 0.9, 400)), 1, 1024).astype(int)
+    out = np.clip(np.rint(rng.lognormal(np.log(240), 0.9, 400)), 1, max_len).astype(int)
+    final = np.minimum(prompt + out, max_len)
+    pow2 = lambda f: min(max_len, 1 << int(np.ceil(np.log2(max(f, 1)))))
+    big = {"paged_block_16": serve_trace(Paged(pa, cap - cap % 16, 16), prompt.tolist(), final.tolist()),
+           "reserve_max": serve_trace(ReserveAhead(cap, lambda f: max_len), prompt.tolist(), final.tolist()),
+           "reserve_pow2": serve_trace(ReserveAhead(cap, pow2), prompt.tolist(), final.tolist()),
+           "reserve_exact": serve_trace(ReserveAhead(cap, lambda f: f), prompt.tolist(), final.tolist())}
+    return {"toy_176_slots": toy, "opt13b_15700_tokens": big}
+
+
 # ---------------------------------------------------------------- main
 def reference_copy_gbs(torch, mib=512, reps=10):
     """Device-to-device copy of `mib` MiB with the runtime's copy (read + write bytes
@@ -692,6 +825,9 @@ def main():
         log(f"cpu oracle: {line['cpu_baseline']['value']} {line['cpu_baseline']['unit']} on {cores} threads")
 
     if not args.no_configs:
+        t0 = time.perf_counter()
+        line["allocator"] = allocator_study(pa)
+        log(f"allocator study: {time.perf_counter() - t0:.1f}s")
         del wl
         torch.cuda.empty_cache()
         entries = []

@@ -330,6 +330,50 @@ pa_status pa_alloc_export(const pa_allocator* a, const int64_t* seq_ids, int32_t
 pa_status pa_alloc_physical_block(const pa_allocator* a, int64_t seq_id, int32_t logical_idx,
                                   int32_t* block_out);
 
+/* ---- prefix caching (KV 缓存与分页注意力 §11 后来的做法: every full block is
+ * identified by its tokens and everything before them, and a new request with
+ * the same beginning reuses the cached blocks; KV Cache从原理到实战 §4.2:
+ * block-level matching, reference counts, LRU eviction that never takes a
+ * block in use).  Identities are 64-bit hashes chained over the blocks,
+ * checked on every hit against the block's tokens and its predecessor's
+ * identity.  A block whose count reaches zero while its identity is held
+ * stays cached (contents kept) in a least-recently-used list; fresh blocks
+ * come from the free list first, then from the LRU end of that list (a
+ * finished sequence's cached blocks enter it last block first).  Blocks of
+ * sequences admitted without token ids are never cached. */
+
+/* New sequence with known token ids (HOST int32 [num_tokens]): reuses the
+ * longest run of leading full blocks whose identities are cached and takes
+ * fresh blocks for the rest; its own new full blocks become findable.
+ * num_cached_out (HOST, may be NULL): tokens already in the cache (a multiple
+ * of block_size) — their keys and values need not be written again.  All or
+ * nothing (PA_ERR_OUT_OF_BLOCKS when short; PA_ERR_EXISTS for a used id). */
+pa_status pa_alloc_add_seq_tokens(pa_allocator* a, int64_t seq_id, const int32_t* tokens,
+                                  int32_t num_tokens, int32_t* num_cached_out);
+
+/* pa_alloc_append_slots with the new tokens' ids (HOST int32 [n]): a block
+ * that its new token fills becomes findable by later sequences.  (A sequence
+ * appended to without ids stops being tracked: its later blocks are not
+ * cached.) */
+pa_status pa_alloc_append_tokens(pa_allocator* a, const int64_t* seq_ids, const int32_t* token_ids,
+                                 int32_t n, int64_t* slot_mapping_out, int32_t* cow_pairs_out,
+                                 int32_t* num_pairs_out);
+
+/* Block accounting.  Utilisation of the KV memory in use (KV 缓存与分页注意力
+ * §05, §07) is filled_slots / (used_blocks * block_size). */
+typedef struct {
+    int64_t num_blocks;
+    int64_t free_blocks;        /* on the free list                               */
+    int64_t evictable_blocks;   /* cached, unreferenced (reusable or evictable)   */
+    int64_t used_blocks;        /* reference count > 0                            */
+    int64_t cached_blocks;      /* identity held (in use or evictable)            */
+    int64_t filled_slots;       /* token slots holding a token, each used block once */
+    int64_t prefix_hit_blocks;  /* blocks reused by admissions so far             */
+    int64_t evictions;          /* cached blocks taken back so far                */
+} pa_alloc_counts;
+pa_status pa_alloc_stats(const pa_allocator* a, pa_alloc_counts* out);
+int32_t pa_alloc_num_evictable(const pa_allocator* a);              /* -1 if a is NULL */
+
 int32_t pa_alloc_num_free(const pa_allocator* a);                   /* -1 if a is NULL */
 int32_t pa_alloc_refcount(const pa_allocator* a, int32_t block);   /* -1 if out of range */
 int32_t pa_alloc_seq_len(const pa_allocator* a, int64_t seq_id);   /* -1 if unknown */

@@ -64,6 +64,12 @@ _SIGNATURES = [
     ("pa_alloc_fork", ctypes.c_int32, [_vp, ctypes.c_int64, ctypes.c_int64]),
     ("pa_alloc_append_slots", ctypes.c_int32,
      [_vp, _c_int64_p, ctypes.c_int32, _c_int64_p, _c_int32_p, _c_int32_p]),
+    ("pa_alloc_add_seq_tokens", ctypes.c_int32,
+     [_vp, ctypes.c_int64, _c_int32_p, ctypes.c_int32, _c_int32_p]),
+    ("pa_alloc_append_tokens", ctypes.c_int32,
+     [_vp, _c_int64_p, _c_int32_p, ctypes.c_int32, _c_int64_p, _c_int32_p, _c_int32_p]),
+    ("pa_alloc_stats", ctypes.c_int32, [_vp, ctypes.c_void_p]),
+    ("pa_alloc_num_evictable", ctypes.c_int32, [_vp]),
     ("pa_alloc_free_seq", ctypes.c_int32, [_vp, ctypes.c_int64]),
     ("pa_alloc_export", ctypes.c_int32,
      [_vp, _c_int64_p, ctypes.c_int32, _c_int32_p, ctypes.c_int32, _c_int32_p]),
@@ -332,6 +338,13 @@ def copy_blocks(k_pools: Sequence, v_pools: Sequence, pairs, *, stream=None) -> 
 
 
 # ------------------------------------------------------------------ host allocator
+class AllocCounts(ctypes.Structure):
+    """pa_alloc_counts of include/pagedattn.h."""
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "num_blocks", "free_blocks", "evictable_blocks", "used_blocks", "cached_blocks",
+        "filled_slots", "prefix_hit_blocks", "evictions")]
+
+
 class BlockAllocator:
     """Host block allocator (free list, reference counts, copy-on-write) in C++."""
 
@@ -362,17 +375,48 @@ class BlockAllocator:
     def fork(self, parent_id: int, child_id: int) -> None:
         _check(lib.pa_alloc_fork(self._h, parent_id, child_id), "alloc_fork")
 
-    def append_slots(self, seq_ids: Sequence[int]) -> Tuple[np.ndarray, np.ndarray]:
+    def add_seq_tokens(self, seq_id: int, tokens: Sequence[int]) -> int:
+        """Admit a sequence with known token ids; returns the tokens already cached."""
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
+        cached = ctypes.c_int32(0)
+        _check(lib.pa_alloc_add_seq_tokens(self._h, seq_id, toks.ctypes.data_as(_c_int32_p),
+                                           len(toks), ctypes.byref(cached)), "alloc_add_seq_tokens")
+        return cached.value
+
+    def append_slots(self, seq_ids: Sequence[int],
+                     token_ids: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
         ids = np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64))
         n = len(ids)
         slots = np.empty(n, dtype=np.int64)
         pairs = np.empty((max(n, 1), 2), dtype=np.int32)
         npairs = ctypes.c_int32(0)
-        _check(lib.pa_alloc_append_slots(self._h, ids.ctypes.data_as(_c_int64_p), n,
-                                         slots.ctypes.data_as(_c_int64_p),
-                                         pairs.ctypes.data_as(_c_int32_p), ctypes.byref(npairs)),
-               "alloc_append_slots")
+        if token_ids is None:
+            _check(lib.pa_alloc_append_slots(self._h, ids.ctypes.data_as(_c_int64_p), n,
+                                             slots.ctypes.data_as(_c_int64_p),
+                                             pairs.ctypes.data_as(_c_int32_p), ctypes.byref(npairs)),
+                   "alloc_append_slots")
+        else:
+            toks = np.ascontiguousarray(np.asarray(token_ids, dtype=np.int32))
+            if len(toks) != n:
+                raise ValueError("one token id per sequence")
+            _check(lib.pa_alloc_append_tokens(self._h, ids.ctypes.data_as(_c_int64_p),
+                                              toks.ctypes.data_as(_c_int32_p), n,
+                                              slots.ctypes.data_as(_c_int64_p),
+                                              pairs.ctypes.data_as(_c_int32_p), ctypes.byref(npairs)),
+                   "alloc_append_tokens")
         return slots, pairs[:npairs.value].copy()
+
+    def stats(self) -> dict:
+        c = AllocCounts()
+        _check(lib.pa_alloc_stats(self._h, ctypes.byref(c)), "alloc_stats")
+        return {n: int(getattr(c, n)) for n, _ in AllocCounts._fields_}
+
+    def utilisation(self) -> float:
+        st = self.stats()
+        return st["filled_slots"] / (st["used_blocks"] * self.block_size) if st["used_blocks"] else 1.0
+
+    def num_evictable(self) -> int:
+        return int(lib.pa_alloc_num_evictable(self._h))
 
     def free_seq(self, seq_id: int) -> None:
         _check(lib.pa_alloc_free_seq(self._h, seq_id), "alloc_free_seq")

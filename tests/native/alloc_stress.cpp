@@ -2,7 +2,9 @@
 // AddressSanitizer and UndefinedBehaviorSanitizer by tests/test_allocator_native.py.
 // After every call the allocator's state is checked against its invariants:
 //   * a block's reference count equals the number of tables that hold it;
-//   * free blocks have count 0, and free + held blocks make up the pool;
+//   * free and cached-unreferenced blocks have count 0, and free + cached +
+//     held blocks make up the pool;
+//   * the counts report agrees (used blocks, evictable blocks);
 //   * a sequence of len tokens holds ceil(len / block_size) blocks;
 //   * export and physical_block report the same tables;
 //   * a failed call changes nothing.
@@ -30,9 +32,10 @@ struct Snapshot {
     std::map<int64_t, int32_t> lens;
     std::vector<int32_t> refs;
     int32_t free_blocks = 0;
+    int32_t evictable = 0;
     bool operator==(const Snapshot& o) const {
         return tables == o.tables && lens == o.lens && refs == o.refs &&
-               free_blocks == o.free_blocks;
+               free_blocks == o.free_blocks && evictable == o.evictable;
     }
 };
 
@@ -51,6 +54,7 @@ Snapshot snapshot(pa_allocator* a, const std::set<int64_t>& ids, int32_t nb) {
     }
     for (int32_t b = 0; b < nb; ++b) s.refs.push_back(pa_alloc_refcount(a, b));
     s.free_blocks = pa_alloc_num_free(a);
+    s.evictable = pa_alloc_num_evictable(a);
     return s;
 }
 
@@ -73,7 +77,12 @@ const char* check(pa_allocator* a, const std::set<int64_t>& ids, int32_t nb, int
         if (s.refs[b] != held[b]) return "reference count != table occurrences";
         used += held[b] > 0;
     }
-    if (used + s.free_blocks != nb) return "free + held != pool";
+    if (used + s.free_blocks + s.evictable != nb) return "free + cached + held != pool";
+    pa_alloc_counts c{};
+    if (pa_alloc_stats(a, &c) != PA_OK) return "stats failed";
+    if (c.used_blocks != used || c.evictable_blocks != s.evictable || c.free_blocks != s.free_blocks ||
+        c.num_blocks != nb || c.cached_blocks < c.evictable_blocks)
+        return "counts disagree";
     // export agrees with physical_block
     if (!ids.empty()) {
         std::vector<int64_t> v(ids.begin(), ids.end());
@@ -119,7 +128,16 @@ int run(uint64_t seed, int steps) {
         if (op == 0 || live.empty()) {                         // new sequence
             const int64_t id = pick(8) == 0 && !live.empty() ? live[pick((int)live.size())]
                                                               : next_id++;
-            st = pa_alloc_add_seq(a, id, pick(3 * bs + 2));
+            if (pick(2) == 0) {
+                st = pa_alloc_add_seq(a, id, pick(3 * bs + 2));
+            } else {                                           // with token ids: prefix cache
+                std::vector<int32_t> toks(pick(3 * bs + 2) + 1);
+                for (auto& t : toks) t = pick(2);
+                int32_t cached = -1;
+                st = pa_alloc_add_seq_tokens(a, id, toks.data(), (int32_t)toks.size() - 1, &cached);
+                if (st == PA_OK && (cached < 0 || cached % bs || cached > (int32_t)toks.size() - 1))
+                    return fail("cached token count", seed, step);
+            }
             if (st == PA_OK) ids.insert(id);
         } else if (op == 1) {                                  // parallel sample
             const int64_t child = next_id++;
@@ -136,8 +154,12 @@ int run(uint64_t seed, int steps) {
             std::vector<int32_t> pairs(2 * (size_t)n + 2, -7);
             int32_t np = -1;
             const bool no_pairs = pick(8) == 0;
-            st = pa_alloc_append_slots(a, batch.data(), n, slots.data(),
-                                       no_pairs ? nullptr : pairs.data(), &np);
+            std::vector<int32_t> toks(n + 1);
+            for (auto& t : toks) t = pick(2);
+            st = pick(2) == 0 ? pa_alloc_append_slots(a, batch.data(), n, slots.data(),
+                                                      no_pairs ? nullptr : pairs.data(), &np)
+                              : pa_alloc_append_tokens(a, batch.data(), toks.data(), n, slots.data(),
+                                                       no_pairs ? nullptr : pairs.data(), &np);
             if (st == PA_OK) {
                 if (np < 0 || np > n) return fail("pair count", seed, step);
                 const Snapshot after = snapshot(a, ids, nb);
@@ -176,7 +198,7 @@ int run(uint64_t seed, int steps) {
     }
     for (int64_t id : std::vector<int64_t>(ids.begin(), ids.end()))
         if (pa_alloc_free_seq(a, id) != PA_OK) return fail("final free", seed, steps);
-    if (pa_alloc_num_free(a) != nb) return fail("blocks leaked", seed, steps);
+    if (pa_alloc_num_free(a) + pa_alloc_num_evictable(a) != nb) return fail("blocks leaked", seed, steps);
     pa_alloc_destroy(a);
     return 0;
 }

@@ -170,3 +170,92 @@ def test_allocator_alive_at_interpreter_exit():
                        timeout=300)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
     assert "Exception ignored" not in r.stderr, r.stderr
+
+
+# ------------------------------------------------------------------ prefix caching, beam search
+def compare_full(lib, model):
+    assert lib.num_free() == model.num_free()
+    assert lib.num_evictable() == model.num_evictable()
+    assert lib.stats() == model.stats()
+    for b in range(model.num_blocks):
+        assert lib.refcount(b) == model.refcount(b)
+    live = sorted(model.tables)
+    assert lib.num_seqs() == len(live)
+    if live:
+        mb = max(1, max(len(model.tables[s]) for s in live))
+        t_lib, l_lib = lib.export(live, mb)
+        t_mod, l_mod = model.export(live, mb)
+        assert np.array_equal(t_lib, t_mod) and np.array_equal(l_lib, l_mod)
+
+
+@settings(max_examples=300, deadline=None)
+@given(seed=st.integers(0, 100_000), nb=st.integers(3, 40), bs=st.sampled_from([1, 2, 4, 16]))
+def test_prefix_cache_differential_against_model(seed, nb, bs):
+    """Admissions with token ids drawn from a 3-symbol vocabulary (so beginnings
+    repeat and blocks are reused), forks, appends with and without token ids,
+    frees: the library and the model make the same decisions (reused tokens,
+    tables, copy-on-write pairs, free and cached lists, counts)."""
+    import random
+    rng = random.Random(seed)
+    order = np.random.default_rng(seed).permutation(nb).astype(np.int32)
+    lib, model = BlockAllocator(nb, bs, order), Allocator(nb, bs, order.tolist())
+    prompts = [[rng.randrange(3) for _ in range(rng.randrange(0, 3 * bs + 2))] for _ in range(4)]
+    nxt = 0
+    for _ in range(40):
+        op = rng.randrange(6)
+        live = sorted(model.tables)
+        if op <= 1 or not live:
+            toks = list(rng.choice(prompts)) + [rng.randrange(3) for _ in range(rng.randrange(3))]
+            try:
+                got_m = model.add_seq_tokens(nxt, toks)
+            except OutOfBlocks:
+                got_m = None
+            if got_m is None:
+                with pytest.raises(PagedAttnError) as e:
+                    lib.add_seq_tokens(nxt, toks)
+                assert e.value.status == -3
+            else:
+                assert lib.add_seq_tokens(nxt, toks) == got_m
+            nxt += 1
+        elif op == 2:
+            p = rng.choice(live)
+            model.fork(p, nxt)
+            lib.fork(p, nxt)
+            nxt += 1
+        elif op in (3, 4):
+            sids = rng.sample(live, rng.randrange(1, len(live) + 1))
+            toks = [rng.randrange(3) for _ in sids] if op == 3 else None
+            try:
+                res_m = model.append_slots(sids, toks)
+            except OutOfBlocks:
+                res_m = None
+            if res_m is None:
+                with pytest.raises(PagedAttnError) as e:
+                    lib.append_slots(sids, toks)
+                assert e.value.status == -3
+            else:
+                slots, pairs = lib.append_slots(sids, toks)
+                assert slots.tolist() == list(res_m[0])
+                assert [tuple(p) for p in pairs.tolist()] == [tuple(p) for p in res_m[1]]
+        else:
+            s = rng.choice(live)
+            model.free_seq(s)
+            lib.free_seq(s)
+        compare_full(lib, model)
+
+
+def test_prefix_cache_reuse_and_eviction_in_the_library():
+    """The pages' rules through the C ABI: same beginning reused, same block after
+    another beginning not reused, cached blocks kept after their sequence ends and
+    taken back least recently used first."""
+    lib = BlockAllocator(6, 2)
+    assert lib.add_seq_tokens(1, [1, 1, 2, 2]) == 0
+    assert lib.add_seq_tokens(2, [1, 1, 2, 2, 3]) == 4
+    assert lib.add_seq_tokens(3, [2, 2, 1, 1]) == 0
+    st0 = lib.stats()
+    assert st0["prefix_hit_blocks"] == 2 and st0["cached_blocks"] == 4
+    lib.free_seq(1)
+    lib.free_seq(2)
+    assert lib.num_evictable() == 2 and lib.stats()["used_blocks"] == 2
+    assert lib.add_seq_tokens(4, [1, 1, 2, 2]) == 4          # taken back from the cache
+    assert lib.num_evictable() == 0

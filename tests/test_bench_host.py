@@ -64,3 +64,56 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_allocator_study_against_closed_forms():
+    """The allocator study's readouts against what the pages' arithmetic fixes:
+    blocks of one token never hold an empty slot (utilisation 1); reserving the
+    maximum of 2,048 tokens in a ~15,700-token cache admits at most 7 requests at
+    once (KV 缓存与分页注意力 §04: 12 GB / 2,048 positions = 7 sequences);
+    utilisation falls as blocks grow (§14) and paged blocks beat every
+    reservation policy (§05, §07)."""
+    import paged_kv_cache_129_amd as pa
+    r = bench.allocator_study(pa)
+    toy, big = r["toy_176_slots"], r["opt13b_15700_tokens"]
+    assert toy["block_1"]["utilisation"] == 1.0
+    u = [toy[f"block_{b}"]["utilisation"] for b in (1, 2, 4, 8, 16)]
+    assert all(x > y for x, y in zip(u, u[1:]))
+    assert toy["reserve_20"]["max_concurrent"] == 176 // 20
+    assert big["reserve_max"]["max_concurrent"] == 15700 // 2048 == 7
+    assert big["paged_block_16"]["utilisation"] > big["reserve_exact"]["utilisation"] > \
+        big["reserve_pow2"]["utilisation"] > big["reserve_max"]["utilisation"]
+    assert big["paged_block_16"]["mean_concurrent"] > big["reserve_exact"]["mean_concurrent"]
+
+
+def test_paged_policy_readout_matches_the_oracle_model():
+    """The study's paged readout comes from the library allocator's counts; the
+    oracle's allocator model, driven through the same trace, gives the same."""
+    import paged_kv_cache_129_amd as pa
+    import oracle
+
+    class ModelPaged(bench.Paged):
+        def __init__(self, capacity, block_size):
+            self.a, self.bs = oracle.Allocator(capacity // block_size, block_size), block_size
+
+        def admit(self, rid, first_len, final_len):
+            try:
+                self.a.add_seq(rid, first_len)
+                return True
+            except oracle.OutOfBlocks:
+                return False
+
+        def grow_all(self, rids):
+            try:
+                if rids:
+                    self.a.append_slots(rids)
+                return True
+            except oracle.OutOfBlocks:
+                return False
+
+    rng = np.random.default_rng(5)
+    finals = rng.integers(1, 21, size=30).tolist()
+    for bs in (1, 4, 16):
+        lib = bench.serve_trace(bench.Paged(pa, 176, bs), [1] * 30, finals)
+        mod = bench.serve_trace(ModelPaged(176, bs), [1] * 30, finals)
+        assert lib == mod
