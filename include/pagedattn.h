@@ -276,6 +276,34 @@ pa_status pa_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num
                          int32_t block_size, int32_t num_blocks,
                          const int32_t* pairs, int32_t num_pairs, void* stream);
 
+/*
+ * swap_blocks — move blocks between pools, e.g. a preempted sequence's blocks
+ * from device pools to pools in pinned host memory and back when it resumes
+ * (KV 缓存与分页注意力 §09 放不下的时候: when blocks run out, the latest
+ * request gives up all of its blocks, which go to CPU memory and come back
+ * later; the data moves unchanged).  For each pair (s, d) and each pool l:
+ * block d of dst_pools[l] = block s of src_pools[l], bit for bit.
+ *
+ *   dst_pools, src_pools  HOST arrays of num_pools pool pointers; each is device
+ *                     memory or pinned host memory known to HIP (hipHostMalloc,
+ *                     torch pin_memory); memory HIP does not know (pageable)
+ *                     gives PA_ERR_INVALID_ARG with nothing enqueued.  16-byte
+ *                     aligned; src and dst must not overlap.
+ *   block_bytes       bytes of one block of one pool (a multiple of 16), e.g.
+ *                     num_kv_heads * block_size * head_dim * element bytes
+ *   dst_num_blocks, src_num_blocks  pool sizes in blocks; pairs with ids
+ *                     outside them (e.g. -1 padding) are skipped
+ *   pairs             DEVICE int32 [num_pairs][2] = (src block, dst block), as
+ *                     pa_alloc_swap_out / pa_alloc_swap_in return (copied to
+ *                     the device); read when the kernel runs.  Destinations
+ *                     must be distinct.
+ * Issue the swap-out copy before any later write into the released device
+ * blocks, and the swap-in copy before the sequence is read (same stream).
+ */
+pa_status pa_swap_blocks(void* const* dst_pools, const void* const* src_pools, int32_t num_pools,
+                         int64_t block_bytes, int32_t dst_num_blocks, int32_t src_num_blocks,
+                         const int32_t* pairs, int32_t num_pairs, void* stream);
+
 /* ------------------------------------------------------------------------
  * Host block allocator: free list, per-block reference counts, block tables
  * and copy-on-write (KV 缓存与分页注意力 §07 块表, §08 共用，写时复制;
@@ -317,6 +345,22 @@ pa_status pa_alloc_append_slots(pa_allocator* a, const int64_t* seq_ids, int32_t
 /* Finished sequence: every block's count drops by one; blocks reaching zero go
  * back to the free list in table order. */
 pa_status pa_alloc_free_seq(pa_allocator* a, int64_t seq_id);
+
+/* Swapping (KV 缓存与分页注意力 §09): a sequence's blocks all move or none do.
+ * swap_out: the sequence leaves `dev` for `host` (an allocator over host
+ * blocks of the same block size): it takes fresh host blocks in the same
+ * logical order and releases its device blocks (a block another sequence
+ * still shares stays with it, its count down by one).  pairs_out HOST int32
+ * [max_pairs][2] receives one (device block, host block) copy per logical
+ * block; PA_ERR_INDEX if max_pairs is smaller than the table, PA_ERR_OUT_OF_BLOCKS
+ * if the host pool is short, and nothing changes on any error.
+ * swap_in: the reverse, (host block, device block) pairs, fresh device blocks.
+ * Prefix-cache tracking of a swapped sequence ends (its blocks come back
+ * uncached). */
+pa_status pa_alloc_swap_out(pa_allocator* dev, pa_allocator* host, int64_t seq_id,
+                            int32_t* pairs_out, int32_t max_pairs, int32_t* num_pairs_out);
+pa_status pa_alloc_swap_in(pa_allocator* dev, pa_allocator* host, int64_t seq_id,
+                           int32_t* pairs_out, int32_t max_pairs, int32_t* num_pairs_out);
 
 /* Block tables HOST int32 [n][max_blocks] (-1 padded) and context lengths HOST
  * int32 [n] of the given sequences.  PA_ERR_INDEX if a table is longer than

@@ -253,6 +253,33 @@ class Allocator:
         del self.lens[seq_id]
         self.tokens.pop(seq_id, None)
 
+    # -- swapping (KV 缓存与分页注意力 §09 放不下的时候): a preempted sequence's blocks
+    # are all moved to CPU memory or none are, and all come back together
+    def swap_out(self, seq_id: int, cpu: "Allocator") -> List[Tuple[int, int]]:
+        """Move a sequence to ``cpu`` (an allocator over host blocks): it gets fresh
+        host blocks in the same logical order and gives up its device blocks.
+        Returns the (device block, host block) copies to make before the device
+        blocks are reused.  Nothing changes if the host pool is short."""
+        table = self._seq(seq_id)
+        if seq_id in cpu.tables:
+            raise ValueError(f"sequence {seq_id} exists on the host")
+        host = cpu.add_seq(seq_id, self.lens[seq_id])
+        pairs = list(zip(table, host))
+        self.free_seq(seq_id)
+        return pairs
+
+    def swap_in(self, seq_id: int, cpu: "Allocator") -> List[Tuple[int, int]]:
+        """Bring a swapped-out sequence back: fresh device blocks in the same logical
+        order; returns the (host block, device block) copies to make before the
+        sequence is read.  Nothing changes if the device pool is short."""
+        host = cpu._seq(seq_id)
+        if seq_id in self.tables:
+            raise ValueError(f"sequence {seq_id} exists on the device")
+        dev = self.add_seq(seq_id, cpu.lens[seq_id])
+        pairs = list(zip(host, dev))
+        cpu.free_seq(seq_id)
+        return pairs
+
     def physical_block(self, seq_id: int, logical_idx: int) -> int:
         table = self._seq(seq_id)
         if logical_idx < 0 or logical_idx >= len(table):

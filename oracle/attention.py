@@ -56,6 +56,16 @@ def copy_blocks(pools: Sequence[np.ndarray], pairs: Sequence[Tuple[int, int]]) -
             p[dst] = p[src].copy()
 
 
+def swap_blocks(dst_pools: Sequence[np.ndarray], src_pools: Sequence[np.ndarray],
+                pairs: Sequence[Tuple[int, int]]) -> None:
+    """Block moves between two pools (device and host): ``dst[d] = src[s]`` for every
+    (s, d) pair and every pool, bytes unchanged (KV 缓存与分页注意力 §09: a
+    preempted sequence's blocks go to CPU memory and come back when it resumes)."""
+    for s, d in pairs:
+        for dst, src in zip(dst_pools, src_pools):
+            dst[d] = src[s].copy()
+
+
 # ------------------------------------------------------------------ gather
 def gather_sequence(pool: np.ndarray, kv_dtype: str, table_row: np.ndarray, n: int,
                     block_size: int, scale: float = 1.0) -> np.ndarray:

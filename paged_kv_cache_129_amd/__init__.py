@@ -57,6 +57,13 @@ _SIGNATURES = [
     ("pa_copy_blocks", ctypes.c_int32,
      [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
+    ("pa_swap_blocks", ctypes.c_int32,
+     [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
+      ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
+    ("pa_alloc_swap_out", ctypes.c_int32,
+     [_vp, _vp, ctypes.c_int64, _c_int32_p, ctypes.c_int32, _c_int32_p]),
+    ("pa_alloc_swap_in", ctypes.c_int32,
+     [_vp, _vp, ctypes.c_int64, _c_int32_p, ctypes.c_int32, _c_int32_p]),
     ("pa_alloc_create", ctypes.c_int32,
      [ctypes.c_int32, ctypes.c_int32, _c_int32_p, ctypes.POINTER(_vp)]),
     ("pa_alloc_destroy", None, [_vp]),
@@ -337,6 +344,52 @@ def copy_blocks(k_pools: Sequence, v_pools: Sequence, pairs, *, stream=None) -> 
                               ctypes.c_void_p(s.cuda_stream)), "copy_blocks")
 
 
+def swap_blocks(dst_pools: Sequence, src_pools: Sequence, pairs, *, stream=None) -> None:
+    """Move block s of every source pool to block d of the matching destination pool
+    for every (s, d) in ``pairs``: device pools and pools in pinned host memory
+    (``pin_memory=True``), in either direction.  ``pairs`` is a device int32 tensor
+    [N, 2] or host pairs (copied to the device on the call's stream)."""
+    torch = _torch()
+    L = len(dst_pools)
+    if L != len(src_pools):
+        raise ValueError("dst_pools and src_pools differ in length")
+    if L == 0:
+        return
+    shape, dt = dst_pools[0].shape[1:], dst_pools[0].dtype
+    for p in list(dst_pools) + list(src_pools):
+        if p.shape[1:] != shape or p.dtype != dt or not p.is_contiguous():
+            raise ValueError("pools must be contiguous and share block shape and dtype")
+    if any(p.shape[0] != dst_pools[0].shape[0] for p in dst_pools) or \
+            any(p.shape[0] != src_pools[0].shape[0] for p in src_pools):
+        raise ValueError("destination pools (and source pools) must hold the same number of blocks")
+        if not (p.is_cuda or p.is_pinned()):
+            raise ValueError("pools must be device tensors or pinned host tensors")
+    dev = next((p.device for p in list(dst_pools) + list(src_pools) if p.is_cuda), None)
+    if dev is None:
+        raise ValueError("one side must be on the device")
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    if isinstance(pairs, torch.Tensor) and pairs.is_cuda:
+        if pairs.dtype != torch.int32 or pairs.dim() != 2 or pairs.shape[1] != 2:
+            raise ValueError("device pairs must be int32 [N, 2]")
+        dpairs = pairs
+    else:
+        host = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+        if len(host) == 0:
+            return
+        if torch.cuda.is_current_stream_capturing():
+            raise ValueError("swap_blocks under graph capture needs device pairs")
+        with torch.cuda.stream(s):
+            dpairs = torch.from_numpy(host).to(dev)
+    if dpairs.shape[0] == 0:
+        return
+    block_bytes = dst_pools[0][0].numel() * dst_pools[0].element_size()
+    dp = (ctypes.c_void_p * L)(*[p.data_ptr() for p in dst_pools])
+    sp = (ctypes.c_void_p * L)(*[p.data_ptr() for p in src_pools])
+    _check(lib.pa_swap_blocks(dp, sp, L, block_bytes, dst_pools[0].shape[0], src_pools[0].shape[0],
+                              _dev(dpairs, "pairs"), dpairs.shape[0], ctypes.c_void_p(s.cuda_stream)),
+           "swap_blocks")
+
+
 # ------------------------------------------------------------------ host allocator
 class AllocCounts(ctypes.Structure):
     """pa_alloc_counts of include/pagedattn.h."""
@@ -405,6 +458,28 @@ class BlockAllocator:
                                               pairs.ctypes.data_as(_c_int32_p), ctypes.byref(npairs)),
                    "alloc_append_tokens")
         return slots, pairs[:npairs.value].copy()
+
+    def _swap(self, fn, host: "BlockAllocator", seq_id: int, where: str) -> np.ndarray:
+        cap = max(1, len(self._table_len_hint(seq_id, host)))
+        pairs = np.empty((cap, 2), dtype=np.int32)
+        n = ctypes.c_int32(0)
+        _check(fn(self._h, host._h, seq_id, pairs.ctypes.data_as(_c_int32_p), cap, ctypes.byref(n)),
+               where)
+        return pairs[:n.value].copy()
+
+    def _table_len_hint(self, seq_id, host):
+        n = max(self.seq_len(seq_id), host.seq_len(seq_id), 0)
+        return range((n + self.block_size - 1) // self.block_size)
+
+    def swap_out(self, seq_id: int, host: "BlockAllocator") -> np.ndarray:
+        """Move a sequence to ``host`` (an allocator over host blocks); returns the
+        (device block, host block) pairs to copy before the device blocks are reused."""
+        return self._swap(lib.pa_alloc_swap_out, host, seq_id, "alloc_swap_out")
+
+    def swap_in(self, seq_id: int, host: "BlockAllocator") -> np.ndarray:
+        """Bring a sequence back from ``host``; returns the (host block, device block)
+        pairs to copy before the sequence is read."""
+        return self._swap(lib.pa_alloc_swap_in, host, seq_id, "alloc_swap_in")
 
     def stats(self) -> dict:
         c = AllocCounts()

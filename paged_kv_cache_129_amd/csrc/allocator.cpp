@@ -280,6 +280,48 @@ pa_status pa_alloc_free_seq(pa_allocator* a, int64_t seq_id) {
     return PA_OK;
 }
 
+pa_status pa_alloc_swap_out(pa_allocator* dev, pa_allocator* host, int64_t seq_id,
+                            int32_t* pairs_out, int32_t max_pairs, int32_t* num_pairs_out) {
+    if (!dev || !host || !num_pairs_out || max_pairs < 0 || dev == host) return PA_ERR_INVALID_ARG;
+    *num_pairs_out = 0;
+    auto it = dev->seqs.find(seq_id);
+    if (it == dev->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+    if (host->seqs.count(seq_id)) return PA_ERR_EXISTS;
+    if (host->block_size != dev->block_size) return PA_ERR_INVALID_ARG;
+    const std::vector<int32_t> table = it->second.blocks;
+    if ((int64_t)table.size() > max_pairs || (!table.empty() && !pairs_out)) return PA_ERR_INDEX;
+    const pa_status st = pa_alloc_add_seq(host, seq_id, it->second.len);   // all or nothing
+    if (st != PA_OK) return st;
+    const std::vector<int32_t>& htab = host->seqs.find(seq_id)->second.blocks;
+    for (size_t k = 0; k < table.size(); ++k) {
+        pairs_out[2 * k] = table[k];
+        pairs_out[2 * k + 1] = htab[k];
+    }
+    *num_pairs_out = (int32_t)table.size();
+    return pa_alloc_free_seq(dev, seq_id);
+}
+
+pa_status pa_alloc_swap_in(pa_allocator* dev, pa_allocator* host, int64_t seq_id,
+                           int32_t* pairs_out, int32_t max_pairs, int32_t* num_pairs_out) {
+    if (!dev || !host || !num_pairs_out || max_pairs < 0 || dev == host) return PA_ERR_INVALID_ARG;
+    *num_pairs_out = 0;
+    auto it = host->seqs.find(seq_id);
+    if (it == host->seqs.end()) return PA_ERR_UNKNOWN_SEQ;
+    if (dev->seqs.count(seq_id)) return PA_ERR_EXISTS;
+    if (host->block_size != dev->block_size) return PA_ERR_INVALID_ARG;
+    const std::vector<int32_t> htab = it->second.blocks;
+    if ((int64_t)htab.size() > max_pairs || (!htab.empty() && !pairs_out)) return PA_ERR_INDEX;
+    const pa_status st = pa_alloc_add_seq(dev, seq_id, it->second.len);     // all or nothing
+    if (st != PA_OK) return st;
+    const std::vector<int32_t>& dtab = dev->seqs.find(seq_id)->second.blocks;
+    for (size_t k = 0; k < htab.size(); ++k) {
+        pairs_out[2 * k] = htab[k];
+        pairs_out[2 * k + 1] = dtab[k];
+    }
+    *num_pairs_out = (int32_t)htab.size();
+    return pa_alloc_free_seq(host, seq_id);
+}
+
 pa_status pa_alloc_export(const pa_allocator* a, const int64_t* seq_ids, int32_t n,
                           int32_t* block_tables_out, int32_t max_blocks,
                           int32_t* context_lens_out) {

@@ -325,6 +325,52 @@ pa_status pa_paged_attention_decode_noalloc(void* out, const void* q, int32_t q_
                        true, stream);
 }
 
+// device-visible address of a pool: device memory as is, pinned host memory
+// (allocated or registered with HIP) through its device mapping; NULL for
+// anything else, pageable host memory included, which a kernel must not touch
+static void* device_view(const void* p) {
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    if (attr.type != hipMemoryTypeDevice && attr.type != hipMemoryTypeHost) return nullptr;
+    return attr.devicePointer;
+}
+
+pa_status pa_swap_blocks(void* const* dst_pools, const void* const* src_pools, int32_t num_pools,
+                         int64_t block_bytes, int32_t dst_num_blocks, int32_t src_num_blocks,
+                         const int32_t* pairs, int32_t num_pairs, void* stream) {
+    if (num_pools < 0 || num_pairs < 0 || block_bytes <= 0 || dst_num_blocks <= 0 ||
+        src_num_blocks <= 0)
+        return PA_ERR_INVALID_ARG;
+    if (block_bytes % 16 != 0) return PA_ERR_UNSUPPORTED;
+    if (num_pools == 0 || num_pairs == 0) return PA_OK;
+    if (!dst_pools || !src_pools || !pairs || (reinterpret_cast<uintptr_t>(pairs) & 7u))
+        return PA_ERR_INVALID_ARG;
+    if ((block_bytes + 4095) / 4096 * (int64_t)num_pairs > INT32_MAX) return PA_ERR_UNSUPPORTED;
+    for (int32_t p0 = 0; p0 < num_pools; p0 += pa::kSwapMaxPools) {
+        pa::SwapArgs a{};
+        a.pairs = pairs;
+        a.block_bytes = block_bytes;
+        a.src_blocks = src_num_blocks;
+        a.dst_blocks = dst_num_blocks;
+        a.num_pairs = num_pairs;
+        a.num_pools = std::min(num_pools - p0, pa::kSwapMaxPools);
+        for (int32_t l = 0; l < a.num_pools; ++l) {
+            void* d = dst_pools[p0 + l] ? device_view(dst_pools[p0 + l]) : nullptr;
+            const void* sv = src_pools[p0 + l] ? device_view(src_pools[p0 + l]) : nullptr;
+            if (!d || !sv || !aligned16(d) || !aligned16(sv)) return PA_ERR_INVALID_ARG;
+            a.dst[l] = d;
+            a.src[l] = sv;
+        }
+        const pa_status st =
+            launch_checked([&] { return pa::launch_swap_blocks(a, as_stream(stream)); });
+        if (st != PA_OK) return st;
+    }
+    return PA_OK;
+}
+
 pa_status pa_paged_attention_prefill(void* out, const void* q, int32_t q_dtype,
                                      const void* k_pool, const void* v_pool, int32_t kv_dtype,
                                      const int32_t* block_tables, int32_t max_blocks_per_seq,

@@ -36,6 +36,19 @@ struct CopyArgs {
 };
 hipError_t launch_copy_blocks(CopyArgs& a, hipStream_t stream);
 
+constexpr int kSwapMaxPools = 64;       // pools per swap launch (pointers in the arguments)
+struct SwapArgs {
+    void* dst[kSwapMaxPools];           // device-visible addresses (device or pinned host)
+    const void* src[kSwapMaxPools];
+    const int32_t* pairs;               // DEVICE int32 [num_pairs][2] = (src block, dst block)
+    int64_t block_bytes;
+    int32_t src_blocks, dst_blocks;     // ids outside these pool sizes are skipped
+    int32_t num_pools;
+    int32_t num_pairs;
+    int32_t slices;                     // set at launch
+};
+hipError_t launch_swap_blocks(SwapArgs& a, hipStream_t stream);
+
 // Sequences are scheduled in windows of kWindow (their metadata is staged in
 // LDS).  The balanced schedule gives each worker (a wavefront) two
 // partial-record slots and one range descriptor per window; a launch has at

@@ -259,3 +259,74 @@ def test_prefix_cache_reuse_and_eviction_in_the_library():
     assert lib.num_evictable() == 2 and lib.stats()["used_blocks"] == 2
     assert lib.add_seq_tokens(4, [1, 1, 2, 2]) == 4          # taken back from the cache
     assert lib.num_evictable() == 0
+
+
+def test_swap_differential_against_model():
+    """Swap-out / swap-in through the C ABI against the model: same pairs, tables,
+    counts on both allocators; all or nothing when a side is short."""
+    import random
+    for seed in range(40):
+        rng = random.Random(seed)
+        bs = rng.choice([1, 2, 4, 16])
+        nd, nh = rng.randrange(2, 30), rng.randrange(1, 30)
+        dev_l, host_l = BlockAllocator(nd, bs), BlockAllocator(nh, bs)
+        dev_m, host_m = Allocator(nd, bs), Allocator(nh, bs)
+        nxt = 0
+        for _ in range(60):
+            op = rng.randrange(5)
+            on_dev, on_host = sorted(dev_m.tables), sorted(host_m.tables)
+            if op == 0 or not (on_dev or on_host):
+                n = rng.randrange(0, 3 * bs)
+                try:
+                    dev_m.add_seq(nxt, n)
+                    ok = True
+                except OutOfBlocks:
+                    ok = False
+                if ok:
+                    dev_l.add_seq(nxt, n)
+                else:
+                    with pytest.raises(PagedAttnError):
+                        dev_l.add_seq(nxt, n)
+                nxt += 1
+            elif op == 1 and on_dev:
+                sid = rng.choice(on_dev)
+                try:
+                    want = dev_m.swap_out(sid, host_m)
+                except OutOfBlocks:
+                    want = None
+                if want is None:
+                    with pytest.raises(PagedAttnError) as e:
+                        dev_l.swap_out(sid, host_l)
+                    assert e.value.status == -3
+                else:
+                    assert [tuple(p) for p in dev_l.swap_out(sid, host_l).tolist()] == want
+            elif op == 2 and on_host:
+                sid = rng.choice(on_host)
+                try:
+                    want = dev_m.swap_in(sid, host_m)
+                except OutOfBlocks:
+                    want = None
+                if want is None:
+                    with pytest.raises(PagedAttnError) as e:
+                        dev_l.swap_in(sid, host_l)
+                    assert e.value.status == -3
+                else:
+                    assert [tuple(p) for p in dev_l.swap_in(sid, host_l).tolist()] == want
+            elif op == 3 and on_dev:
+                sid = rng.choice(on_dev)
+                try:
+                    want = dev_m.append_slots([sid])
+                except OutOfBlocks:
+                    want = None
+                if want is None:
+                    with pytest.raises(PagedAttnError):
+                        dev_l.append_slots([sid])
+                else:
+                    dev_l.append_slots([sid])
+            elif op == 4 and on_dev:
+                sid = rng.choice(on_dev)
+                dev_m.fork(sid, nxt)
+                dev_l.fork(sid, nxt)
+                nxt += 1
+            for lib, model in ((dev_l, dev_m), (host_l, host_m)):
+                compare_full(lib, model)

@@ -198,3 +198,55 @@ def test_random_operation_sequences_keep_invariants(ops, bs, nb):
         except (OutOfBlocks, UnknownSequence, ValueError):
             pass
         check_invariants(a)
+
+
+# ------------------------------------------------------------------ swapping (§09)
+def test_swap_out_and_in_keeps_contents_and_order():
+    """A preempted sequence's blocks all go to the host and all come back (KV 缓存与
+    分页注意力 §09); the data moves bit for bit and the logical order is kept, so
+    the sequence reads back the same tokens from new physical blocks."""
+    gpu, cpu = Allocator(12, 4), Allocator(6, 4)
+    gpu.add_seq(1, 10)                        # 3 blocks
+    gpu.add_seq(2, 5)
+    rng = np.random.default_rng(0)
+    dev = rng.integers(0, 255, size=(12, 4, 8), dtype=np.uint8)
+    host = np.zeros((6, 4, 8), dtype=np.uint8)
+    before = [dev[gpu.physical_block(1, k)].copy() for k in range(3)]
+    pairs = gpu.swap_out(1, cpu)
+    oracle.swap_blocks([host], [dev], pairs)
+    assert 1 not in gpu.tables and cpu.lens[1] == 10 and gpu.num_free() == 12 - 2
+    dev[[b for b, _ in pairs]] = 0            # the device blocks are reused by others
+    back = gpu.swap_in(1, cpu)
+    oracle.swap_blocks([dev], [host], back)
+    assert cpu.num_free() == 6 and gpu.lens[1] == 10
+    after = [dev[gpu.physical_block(1, k)] for k in range(3)]
+    assert all(np.array_equal(x, y) for x, y in zip(before, after))
+
+
+def test_swap_is_all_or_nothing():
+    gpu, cpu = Allocator(8, 4), Allocator(2, 4)
+    gpu.add_seq(1, 12)                        # 3 blocks, host has 2
+    state = (list(gpu.free), list(gpu.ref), dict(gpu.lens))
+    with pytest.raises(OutOfBlocks):
+        gpu.swap_out(1, cpu)
+    assert (list(gpu.free), list(gpu.ref), dict(gpu.lens)) == state and not cpu.tables
+    gpu2 = Allocator(3, 4)
+    cpu2 = Allocator(8, 4)
+    gpu2.add_seq(1, 12)
+    gpu2.swap_out(1, cpu2)
+    gpu2.add_seq(2, 1)                        # the device pool is now short for 1
+    with pytest.raises(OutOfBlocks):
+        gpu2.swap_in(1, cpu2)
+    assert 1 in cpu2.tables and 1 not in gpu2.tables
+
+
+def test_swap_of_a_shared_sequence_keeps_the_sharer():
+    """Swapping out one of two parallel samples leaves the other's blocks in place
+    (counts drop by one); the swapped one gets its own copies."""
+    gpu, cpu = Allocator(8, 4), Allocator(8, 4)
+    gpu.add_seq(1, 6)
+    gpu.fork(1, 2)
+    shared = list(gpu.tables[1])
+    pairs = gpu.swap_out(2, cpu)
+    assert [g for g, _ in pairs] == shared and all(gpu.refcount(b) == 1 for b in shared)
+    assert gpu.tables[1] == shared
