@@ -26,9 +26,11 @@ Every function is pinned by tests under ``tests/`` against things other than
 itself: values printed on the pages, brute force, closed forms, invariants and
 library routines.  Nothing here is "parity unpinned".
 """
-from .formats import (decode, e4m3_decode_table, e4m3_encode, e4m3_values)  # noqa: F401
+from .formats import (decode, e4m3_decode_table, e4m3_encode, e4m3_values,  # noqa: F401
+                      int8_group_encode)
 from .attention import (gather_sequence, paged_attention, contiguous_attention,  # noqa: F401
-                        partition_states, lse_combine, kv_write, copy_blocks, swap_blocks)
+                        partition_states, lse_combine, kv_write, kv_write_int8, copy_blocks,
+                        swap_blocks)
 from .prefill import paged_prefill, query_positions  # noqa: F401
 from .allocator import Allocator, OutOfBlocks, UnknownSequence, RefcountError  # noqa: F401
 from .sizes import kv_bytes_per_token  # noqa: F401

@@ -11,7 +11,7 @@ from typing import List, Sequence, Tuple
 
 import numpy as np
 
-from .formats import decode, e4m3_encode
+from .formats import decode, e4m3_encode, int8_group_encode
 
 
 # ------------------------------------------------------------------ cache write
@@ -41,6 +41,24 @@ def kv_write(k_pool: np.ndarray, v_pool: np.ndarray, kv_dtype: str,
                 pool[b, :, o, :] = e4m3_encode(x * inv)
             else:
                 raise ValueError(f"unsupported write {src_dtype}->{kv_dtype}")
+
+
+def kv_write_int8(k_pool: np.ndarray, v_pool: np.ndarray, k_scales: np.ndarray,
+                  v_scales: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, src_dtype: str,
+                  slot_mapping: Sequence[int], block_size: int) -> None:
+    """Cache write into an int8 cache with a scale per (token, KV head): each new
+    token's head vector is quantised on its own (group-wise 8-bit integers,
+    KV Cache从原理到实战 §5.2) and stored with its scale at the token's slot.
+    Pools [NB, Hkv, bs, D] int8, scale pools [NB, Hkv, bs] float32."""
+    num_slots = k_pool.shape[0] * block_size
+    for i, slot in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+        if slot < 0 or slot >= num_slots:
+            continue
+        b, o = divmod(int(slot), block_size)
+        for pool, scales, new in ((k_pool, k_scales, k_new), (v_pool, v_scales, v_new)):
+            code, scale = int8_group_encode(decode(new[i], src_dtype).astype(np.float32))
+            pool[b, :, o, :] = code
+            scales[b, :, o] = scale
 
 
 # ------------------------------------------------------------------ copy on write
@@ -78,6 +96,8 @@ def gather_sequence(pool: np.ndarray, kv_dtype: str, table_row: np.ndarray, n: i
     t = np.arange(n)
     blocks = np.asarray(table_row)[t // block_size]
     raw = pool[blocks, :, t % block_size, :]
+    if kv_dtype == "int8":                   # scale: the [NB, Hkv, bs] pool of group scales
+        return decode(raw, kv_dtype, np.asarray(scale)[blocks, :, t % block_size])
     return decode(raw, kv_dtype, scale)
 
 

@@ -1,4 +1,5 @@
-"""Storage formats -> float64, and the 8-bit float (e4m3) codec.
+"""Storage formats -> float64, the 8-bit float (e4m3) codec and the group-wise
+8-bit integer codec.
 
 The pages say an fp8 cache stores each number in one byte and fits about
 twice the tokens (KV 缓存与分页注意力 §11; KV Cache内存优化技术原理与
@@ -64,8 +65,32 @@ def e4m3_encode(y: np.ndarray) -> np.ndarray:
     return code.astype(np.uint8)
 
 
-def decode(a: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
-    """Storage array -> float64 values (exact widening; fp8 times its scale)."""
+INT8_MAX = 127
+
+
+def int8_group_encode(x: np.ndarray):
+    """float32 values [..., group] -> (int8 codes [..., group], float32 scales [...]).
+
+    Group-wise symmetric 8-bit integers (KV Cache从原理到实战 §5.2: a scale per
+    group of numbers, e.g. 128): here a group is one token's head vector.  In
+    float32, as written: amax = max |x| over the group; scale = amax / 127;
+    code = x / scale rounded to the nearest integer, ties to even, clamped to
+    [-127, 127]; a group of zeros has scale 0 and codes 0.  Value = code * scale.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    scale = (amax / np.float32(INT8_MAX)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    q = (x / safe[..., None]).astype(np.float32)
+    code = np.clip(np.rint(q), -INT8_MAX, INT8_MAX)
+    code = np.where(scale[..., None] > 0, code, 0).astype(np.int8)
+    return code, scale
+
+
+def decode(a: np.ndarray, dtype: str, scale=1.0) -> np.ndarray:
+    """Storage array -> float64 values (exact widening; fp8 times its scale; int8
+    times its group's scale, ``scale`` then being an array of one scale per group,
+    i.e. ``a.shape[:-1]``)."""
     a = np.asarray(a)
     if dtype == "f32":
         return a.astype(np.float32).astype(np.float64)
@@ -76,4 +101,6 @@ def decode(a: np.ndarray, dtype: str, scale: float = 1.0) -> np.ndarray:
         return bits.view(np.float32).astype(np.float64)
     if dtype == "fp8_e4m3":
         return _TABLE[a.view(np.uint8)] * float(scale)
+    if dtype == "int8":
+        return a.view(np.int8).astype(np.float64) * np.asarray(scale, dtype=np.float32).astype(np.float64)[..., None]
     raise ValueError(dtype)
