@@ -45,7 +45,9 @@ typedef enum {
     PA_F32 = 0,
     PA_F16 = 1,
     PA_BF16 = 2,
-    PA_FP8_E4M3 = 3   /* OCP E4M3FN: bias 7, max 448, no inf, NaN = S.1111.111 */
+    PA_FP8_E4M3 = 3,  /* OCP E4M3FN: bias 7, max 448, no inf, NaN = S.1111.111 */
+    PA_INT8 = 4       /* group-wise int8 cache: codes in [-127, 127], one float32
+                         scale per (token, KV head) in separate scale pools */
 } pa_dtype;
 
 typedef enum {
@@ -74,7 +76,8 @@ const char* pa_last_error(void);
 /*
  * Per-token KV-cache bytes: 2 x (num_kv_heads x head_dim) x num_layers x
  * bytes-per-number — one key and one value per layer (KV 缓存与分页注意力
- * §03 一个词元 800 KB; KV Cache从原理到实战 §2.2 KV Cache的显存账).
+ * §03 一个词元 800 KB; KV Cache从原理到实战 §2.2 KV Cache的显存账); for
+ * PA_INT8 each key and value head vector adds its 4-byte scale.
  * Returns -1 for a non-positive size or an unknown dtype.
  */
 int64_t pa_kv_bytes_per_token(int32_t num_kv_heads, int32_t head_dim, int32_t num_layers,
@@ -96,7 +99,8 @@ int64_t pa_kv_bytes_per_token(int32_t num_kv_heads, int32_t head_dim, int32_t nu
  *   with 1/scale computed in fp32 on the host, saturating to +-448, rounding
  *   to nearest even, NaN kept as NaN (KV 缓存与分页注意力 §11: 8-bit floats,
  *   one byte per number).  k_scale/v_scale are ignored for non-fp8 pools and
- *   must be finite and > 0 for fp8.
+ *   must be finite and > 0 for fp8.  PA_INT8 pools carry scale pools and are
+ *   written by pa_kv_cache_write_int8 (PA_ERR_UNSUPPORTED here).
  *   num_tokens == 0 is a no-op.
  */
 pa_status pa_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype,
@@ -104,6 +108,32 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dt
                             const int64_t* slot_mapping, int32_t num_tokens,
                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                             int32_t num_blocks, float k_scale, float v_scale, void* stream);
+
+/*
+ * kv_cache_write_int8 — the cache write into a group-wise int8 cache
+ * (KV Cache从原理到实战 §5.2 量化: 8-bit integers with one scale per group of
+ * numbers; here a group is one token's head vector, so every key and value
+ * vector carries its own scale).  For each new token i with a valid slot and
+ * each KV head g, separately for K and V, in float32:
+ *     amax  = max_d |x[i][g][d]|,   scale = amax / 127 (correctly rounded)
+ *     code  = x / scale rounded to nearest, ties to even, clamped to [-127, 127]
+ *             (all codes 0 and scale 0 for an all-zero vector)
+ * stored as pool[block][g][offset][d] = code and scales[block][g][offset] = scale;
+ * the value a code stands for is code * scale.
+ *
+ *   k_new, v_new      DEVICE, dense [num_tokens][num_kv_heads][head_dim], src_dtype
+ *                     in {F32, F16, BF16}; non-finite inputs give unspecified codes
+ *   k_pool, v_pool    DEVICE int8 pools, pool layout above (16-byte aligned)
+ *   k_scales, v_scales DEVICE float32 [num_blocks][num_kv_heads][block_size]
+ *   slot_mapping      DEVICE int64 [num_tokens], as for pa_kv_cache_write
+ * Copy-on-write and swapping of an int8 cache move its scale pools as well:
+ * pass them to pa_copy_blocks as PA_F32 pools with head_dim 1.
+ */
+pa_status pa_kv_cache_write_int8(const void* k_new, const void* v_new, int32_t src_dtype,
+                                 void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                                 const int64_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, void* stream);
 
 /* partition_size value that selects the balanced split (see below) */
 #define PA_PARTITION_BALANCED (-1)
@@ -133,7 +163,8 @@ size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, in
  *                  (rounded to nearest even from fp32 accumulators)
  *   q              DEVICE [num_seqs][num_heads][head_dim], q_dtype in {F32, F16, BF16}
  *   k_pool, v_pool DEVICE, pool layout above, kv_dtype.  Supported pairs:
- *                  kv == q, or kv == PA_FP8_E4M3 with q in {F32, F16, BF16}.
+ *                  kv == q, or kv == PA_FP8_E4M3 with q in {F32, F16, BF16}
+ *                  (PA_INT8 pools: pa_paged_attention_decode_int8).
  *   block_tables   DEVICE int32 [num_seqs][max_blocks_per_seq]; entries past
  *                  ceil(n / block_size) are never read.  An entry outside
  *                  [0, num_blocks) makes its tokens count as absent (never read).
@@ -171,6 +202,27 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
                                     float scale, float k_scale, float v_scale,
                                     int32_t partition_size, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_decode_int8 — pa_paged_attention_decode over an int8 cache
+ * written by pa_kv_cache_write_int8: K_s[t][g] and V_s[t][g] are the codes
+ * times their own scales, k_scales / v_scales [block][g][offset] (same layout
+ * and scale pools as the write).  q_dtype in {F32, F16, BF16}; out in q_dtype.
+ * Every other argument, the workspace (pa_paged_attention_workspace_size)
+ * and the limits are as for pa_paged_attention_decode.  The scale is applied
+ * to each token's dot product and to its softmax weight, so the codes are
+ * never widened to another cache format.
+ */
+pa_status pa_paged_attention_decode_int8(void* out, const void* q, int32_t q_dtype,
+                                         const void* k_pool, const void* v_pool,
+                                         const float* k_scales, const float* v_scales,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t max_context_len,
+                                         int32_t num_seqs, int32_t num_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int32_t num_blocks, float scale,
+                                         int32_t partition_size, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /*
  * paged_attention_prefill — multi-token attention over a paged cache: the

@@ -19,8 +19,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpagedattn.so")
 
-PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3 = 0, 1, 2, 3
-DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3}
+PA_F32, PA_F16, PA_BF16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3, 4
+DTYPE_CODES = {"f32": PA_F32, "f16": PA_F16, "bf16": PA_BF16, "fp8_e4m3": PA_FP8_E4M3,
+               "int8": PA_INT8}
 STATUS = {0: "PA_OK", -1: "PA_ERR_INVALID_ARG", -2: "PA_ERR_UNSUPPORTED",
           -3: "PA_ERR_OUT_OF_BLOCKS", -4: "PA_ERR_INDEX", -5: "PA_ERR_UNKNOWN_SEQ",
           -6: "PA_ERR_REFCOUNT", -7: "PA_ERR_HIP", -8: "PA_ERR_WORKSPACE", -9: "PA_ERR_EXISTS"}
@@ -39,7 +40,14 @@ _SIGNATURES = [
      [_vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
       ctypes.c_float, ctypes.c_float, _vp]),
+    ("pa_kv_cache_write_int8", ctypes.c_int32,
+     [_vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, ctypes.c_int32,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp]),
     ("pa_paged_attention_workspace_size", ctypes.c_size_t, [ctypes.c_int32] * 6),
+    ("pa_paged_attention_decode_int8", ctypes.c_int32,
+     [_vp, _vp, ctypes.c_int32, _vp, _vp, _vp, _vp, _vp, ctypes.c_int32, _vp,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+      ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_int32, _vp, ctypes.c_size_t, _vp]),
     ("pa_paged_attention_decode", ctypes.c_int32,
      [_vp, _vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp, ctypes.c_int32, _vp,
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -138,7 +146,7 @@ def _torch():
 def dtype_code(t) -> int:
     torch = _torch()
     m = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16,
-         torch.uint8: PA_FP8_E4M3}
+         torch.uint8: PA_FP8_E4M3, torch.int8: PA_INT8}
     fp8 = getattr(torch, "float8_e4m3fn", None)
     if fp8 is not None:
         m[fp8] = PA_FP8_E4M3
@@ -196,6 +204,31 @@ def kv_cache_write(k_new, v_new, k_pool, v_pool, slot_mapping, *, k_scale: float
            "kv_cache_write")
 
 
+def kv_cache_write_int8(k_new, v_new, k_pool, v_pool, k_scales, v_scales, slot_mapping, *,
+                        stream=None) -> None:
+    """Quantise new tokens' K/V ([T, Hkv, D]) into int8 [NB, Hkv, bs, D] pools, one
+    float32 scale per (token, KV head) into [NB, Hkv, bs] scale pools."""
+    torch = _torch()
+    T, Hkv, D = k_new.shape
+    NB, Hkv2, bs, D2 = k_pool.shape
+    if (Hkv, D) != (Hkv2, D2) or v_new.shape != k_new.shape or v_pool.shape != k_pool.shape:
+        raise ValueError("shape mismatch")
+    if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
+        raise ValueError("int8 pools expected")
+    for sc in (k_scales, v_scales):
+        if sc.dtype != torch.float32 or tuple(sc.shape) != (NB, Hkv, bs):
+            raise ValueError("scale pools must be float32 [NB, Hkv, bs]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    _same_dtype(k_new, v_new, "k_new", "v_new")
+    _one_device(k_new, v_new, k_pool, v_pool, k_scales, v_scales, slot_mapping)
+    _check(lib.pa_kv_cache_write_int8(
+        _dev(k_new, "k_new"), _dev(v_new, "v_new"), dtype_code(k_new), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"), _dev(k_scales, "k_scales"), _dev(v_scales, "v_scales"),
+        _dev(slot_mapping, "slot_mapping"), T, Hkv, D, bs, NB, _stream(stream, k_pool.device)),
+        "kv_cache_write_int8")
+
+
 PARTITION_BALANCED = -1
 
 
@@ -242,6 +275,42 @@ def paged_attention_decode(out, q, k_pool, v_pool, block_tables, context_lens, *
         block_tables.shape[1], _dev(context_lens, "context_lens"), int(max_context_len), S, H,
         Hkv, D, bs, NB, float(scale), float(k_scale), float(v_scale), int(partition_size),
         ws_ptr, ws_bytes, _stream(stream, q.device)), "paged_attention_decode")
+
+
+def paged_attention_decode_int8(out, q, k_pool, v_pool, k_scales, v_scales, block_tables,
+                                context_lens, *, max_context_len: int, scale: float,
+                                partition_size: int = 0, workspace=None, stream=None) -> None:
+    """paged_attention_decode over int8 [NB, Hkv, bs, D] pools with float32
+    [NB, Hkv, bs] scale pools (as written by kv_cache_write_int8)."""
+    torch = _torch()
+    S, H, D = q.shape
+    NB, Hkv, bs, D2 = k_pool.shape
+    if D2 != D or out.shape != q.shape or out.dtype != q.dtype or v_pool.shape != k_pool.shape:
+        raise ValueError("shape mismatch")
+    if k_pool.dtype != torch.int8 or v_pool.dtype != torch.int8:
+        raise ValueError("int8 pools expected")
+    for sc in (k_scales, v_scales):
+        if sc.dtype != torch.float32 or tuple(sc.shape) != (NB, Hkv, bs):
+            raise ValueError("scale pools must be float32 [NB, Hkv, bs]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [S, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
+        raise ValueError("context_lens must be int32 [S]")
+    _one_device(out, q, k_pool, v_pool, k_scales, v_scales, block_tables, context_lens,
+                *([workspace] if workspace is not None else []))
+    need = paged_attention_workspace_size(S, H, Hkv, D, max_context_len, partition_size)
+    if need and workspace is None:
+        with torch.cuda.stream(stream if stream is not None else torch.cuda.current_stream(q.device)):
+            workspace = new_workspace(need, q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else ctypes.c_void_p(0)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.pa_paged_attention_decode_int8(
+        _dev(out, "out"), _dev(q, "q"), dtype_code(q), _dev(k_pool, "k_pool"),
+        _dev(v_pool, "v_pool"), _dev(k_scales, "k_scales"), _dev(v_scales, "v_scales"),
+        _dev(block_tables, "block_tables"), block_tables.shape[1],
+        _dev(context_lens, "context_lens"), int(max_context_len), S, H, Hkv, D, bs, NB,
+        float(scale), int(partition_size), ws_ptr, ws_bytes, _stream(stream, q.device)),
+        "paged_attention_decode_int8")
 
 
 def paged_attention_prefill(out, q, k_pool, v_pool, block_tables, context_lens, query_start, *,
@@ -307,14 +376,18 @@ def copy_blocks(k_pools: Sequence, v_pools: Sequence, pairs, *, stream=None) -> 
     runs: a captured launch replays with whatever the buffer holds; rows with
     an id outside the pool, e.g. -1 padding, are skipped), or host pairs
     (a sequence or array), which are copied to the device on the call's stream
-    first."""
+    first.  Pools are [NB, Hkv, bs, D], or the [NB, Hkv, bs] float32 scale pools
+    of an int8 cache."""
     torch = _torch()
     L = len(k_pools)
     if L != len(v_pools):
         raise ValueError("k_pools and v_pools differ in length")
     if L == 0:
         return
-    NB, Hkv, bs, D = k_pools[0].shape
+    if k_pools[0].dim() == 3:               # int8 scale pools [NB, Hkv, bs]: head_dim 1
+        (NB, Hkv, bs), D = k_pools[0].shape, 1
+    else:
+        NB, Hkv, bs, D = k_pools[0].shape
     for p in list(k_pools) + list(v_pools):
         if p.shape != k_pools[0].shape or p.dtype != k_pools[0].dtype:
             raise ValueError("all pools must share shape and dtype")
@@ -362,6 +435,7 @@ def swap_blocks(dst_pools: Sequence, src_pools: Sequence, pairs, *, stream=None)
     if any(p.shape[0] != dst_pools[0].shape[0] for p in dst_pools) or \
             any(p.shape[0] != src_pools[0].shape[0] for p in src_pools):
         raise ValueError("destination pools (and source pools) must hold the same number of blocks")
+    for p in list(dst_pools) + list(src_pools):
         if not (p.is_cuda or p.is_pinned()):
             raise ValueError("pools must be device tensors or pinned host tensors")
     dev = next((p.device for p in list(dst_pools) + list(src_pools) if p.is_cuda), None)

@@ -15,7 +15,7 @@
 
 namespace {
 
-bool valid_dtype(int32_t dt) { return dt >= PA_F32 && dt <= PA_FP8_E4M3; }
+bool valid_dtype(int32_t dt) { return dt >= PA_F32 && dt <= PA_INT8; }
 
 int log2_exact(int32_t v) {
     if (v <= 0 || (v & (v - 1))) return -1;
@@ -107,7 +107,9 @@ const char* pa_last_error(void) { return g_last_error; }
 int64_t pa_kv_bytes_per_token(int32_t num_kv_heads, int32_t head_dim, int32_t num_layers,
                               int32_t dtype) {
     if (num_kv_heads <= 0 || head_dim <= 0 || num_layers <= 0 || !valid_dtype(dtype)) return -1;
-    return 2 * (int64_t)num_kv_heads * head_dim * num_layers * pa::elem_bytes(dtype);
+    const int64_t per_head = (int64_t)head_dim * pa::elem_bytes(dtype) +
+                             (dtype == PA_INT8 ? (int64_t)sizeof(float) : 0);   // + the scale
+    return 2 * (int64_t)num_kv_heads * num_layers * per_head;
 }
 
 pa_status pa_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dtype,
@@ -121,6 +123,7 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dt
     const int lbs = log2_exact(block_size);
     if (lbs < 0 || lbs > 8) return PA_ERR_INVALID_ARG;
     if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+    if (src_dtype == PA_INT8 || kv_dtype == PA_INT8) return PA_ERR_UNSUPPORTED;   // scale pools
     const bool quantise = kv_dtype == PA_FP8_E4M3 && src_dtype != PA_FP8_E4M3;
     if (src_dtype != kv_dtype && !quantise) return PA_ERR_UNSUPPORTED;
     if (quantise && !(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) &&
@@ -144,6 +147,41 @@ pa_status pa_kv_cache_write(const void* k_new, const void* v_new, int32_t src_dt
     a.k_inv_scale = quantise ? 1.0f / k_scale : 1.0f;     // IEEE fp32 division
     a.v_inv_scale = quantise ? 1.0f / v_scale : 1.0f;
     return launch_checked([&] { return pa::launch_kv_write(a, src_dtype, kv_dtype, as_stream(stream)); });
+}
+
+pa_status pa_kv_cache_write_int8(const void* k_new, const void* v_new, int32_t src_dtype,
+                                 void* k_pool, void* v_pool, float* k_scales, float* v_scales,
+                                 const int64_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int32_t num_blocks, void* stream) {
+    if (src_dtype != PA_F32 && src_dtype != PA_F16 && src_dtype != PA_BF16)
+        return valid_dtype(src_dtype) ? PA_ERR_UNSUPPORTED : PA_ERR_INVALID_ARG;
+    if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
+        return PA_ERR_INVALID_ARG;
+    const int lbs = log2_exact(block_size);
+    if (lbs < 0 || lbs > 8) return PA_ERR_INVALID_ARG;
+    if (!supported_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+    if ((int64_t)num_tokens * num_kv_heads > ((int64_t)1 << 33)) return PA_ERR_UNSUPPORTED;
+    if (num_tokens == 0) return PA_OK;
+    if (!k_new || !v_new || !k_pool || !v_pool || !k_scales || !v_scales || !slot_mapping)
+        return PA_ERR_INVALID_ARG;
+    if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        (reinterpret_cast<uintptr_t>(k_scales) & 3u) || (reinterpret_cast<uintptr_t>(v_scales) & 3u))
+        return PA_ERR_INVALID_ARG;
+    pa::WriteArgs a{};
+    a.k_new = k_new;
+    a.v_new = v_new;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
+    a.slot_mapping = slot_mapping;
+    a.num_tokens = num_tokens;
+    a.num_kv_heads = num_kv_heads;
+    a.head_dim = head_dim;
+    a.log2_bs = lbs;
+    a.num_slots = (int64_t)num_blocks * block_size;
+    return launch_checked([&] { return pa::launch_kv_write(a, src_dtype, PA_INT8, as_stream(stream)); });
 }
 
 size_t pa_paged_attention_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -202,9 +240,12 @@ pa_status decode_impl(void* out, const void* q, int32_t q_dtype,
                                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                     float scale, float k_scale, float v_scale,
+                                    const float* k_scales, const float* v_scales,
                                     int32_t partition_size, void* workspace,
                                     size_t workspace_bytes, bool use_scratch, void* stream) {
     if (!valid_dtype(q_dtype) || !valid_dtype(kv_dtype)) return PA_ERR_INVALID_ARG;
+    // int8 caches come with their scale pools (pa_paged_attention_decode_int8) and only then
+    if ((kv_dtype == PA_INT8) != (k_scales != nullptr)) return PA_ERR_UNSUPPORTED;
     if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
         num_blocks <= 0 || max_blocks_per_seq <= 0 || max_context_len < 0 ||
         (partition_size < 0 && partition_size != PA_PARTITION_BALANCED))
@@ -213,8 +254,9 @@ pa_status decode_impl(void* out, const void* q, int32_t q_dtype,
     const int lbs = log2_exact(block_size);
     if (lbs < 0 || lbs > 8) return PA_ERR_INVALID_ARG;
     if (!std::isfinite(scale)) return PA_ERR_INVALID_ARG;
-    if (q_dtype == PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
-    if (kv_dtype != q_dtype && kv_dtype != PA_FP8_E4M3) return PA_ERR_UNSUPPORTED;
+    if (q_dtype == PA_FP8_E4M3 || q_dtype == PA_INT8) return PA_ERR_UNSUPPORTED;
+    if (kv_dtype != q_dtype && kv_dtype != PA_FP8_E4M3 && kv_dtype != PA_INT8)
+        return PA_ERR_UNSUPPORTED;
     if (kv_dtype == PA_FP8_E4M3 && !(std::isfinite(k_scale) && k_scale > 0.0f &&
                                      std::isfinite(v_scale) && v_scale > 0.0f))
         return PA_ERR_INVALID_ARG;
@@ -223,6 +265,9 @@ pa_status decode_impl(void* out, const void* q, int32_t q_dtype,
     if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
         return PA_ERR_INVALID_ARG;
     if (!aligned16(out) || !aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool))
+        return PA_ERR_INVALID_ARG;
+    if (kv_dtype == PA_INT8 && (!v_scales || (reinterpret_cast<uintptr_t>(k_scales) & 3u) ||
+                                (reinterpret_cast<uintptr_t>(v_scales) & 3u)))
         return PA_ERR_INVALID_ARG;
 
     const int64_t cap64 = std::min<int64_t>(max_context_len, (int64_t)max_blocks_per_seq << lbs);
@@ -265,6 +310,8 @@ pa_status decode_impl(void* out, const void* q, int32_t q_dtype,
     a.v_pool = v_pool;
     a.tables = block_tables;
     a.ctx_lens = context_lens;
+    a.k_scales = k_scales;
+    a.v_scales = v_scales;
     a.ws = reinterpret_cast<float*>(workspace);
     a.nrec = (int64_t)num_seqs * num_heads * parts;     // balanced: set with the grid
     a.rec_capacity = rec_capacity;
@@ -305,8 +352,25 @@ pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,
                                     size_t workspace_bytes, void* stream) {
     return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq,
                        context_lens, max_context_len, num_seqs, num_heads, num_kv_heads, head_dim,
-                       block_size, num_blocks, scale, k_scale, v_scale, partition_size, workspace,
-                       workspace_bytes, false, stream);
+                       block_size, num_blocks, scale, k_scale, v_scale, nullptr, nullptr,
+                       partition_size, workspace, workspace_bytes, false, stream);
+}
+
+pa_status pa_paged_attention_decode_int8(void* out, const void* q, int32_t q_dtype,
+                                         const void* k_pool, const void* v_pool,
+                                         const float* k_scales, const float* v_scales,
+                                         const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                         const int32_t* context_lens, int32_t max_context_len,
+                                         int32_t num_seqs, int32_t num_heads,
+                                         int32_t num_kv_heads, int32_t head_dim,
+                                         int32_t block_size, int32_t num_blocks, float scale,
+                                         int32_t partition_size, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    if (!k_scales) return PA_ERR_INVALID_ARG;
+    return decode_impl(out, q, q_dtype, k_pool, v_pool, PA_INT8, block_tables, max_blocks_per_seq,
+                       context_lens, max_context_len, num_seqs, num_heads, num_kv_heads, head_dim,
+                       block_size, num_blocks, scale, 1.0f, 1.0f, k_scales, v_scales,
+                       partition_size, workspace, workspace_bytes, false, stream);
 }
 
 pa_status pa_paged_attention_decode_noalloc(void* out, const void* q, int32_t q_dtype,
@@ -321,8 +385,8 @@ pa_status pa_paged_attention_decode_noalloc(void* out, const void* q, int32_t q_
                                             void* stream) {
     return decode_impl(out, q, q_dtype, k_pool, v_pool, kv_dtype, block_tables, max_blocks_per_seq,
                        context_lens, max_context_len, num_seqs, num_heads, num_kv_heads, head_dim,
-                       block_size, num_blocks, scale, k_scale, v_scale, partition_size, nullptr, 0,
-                       true, stream);
+                       block_size, num_blocks, scale, k_scale, v_scale, nullptr, nullptr,
+                       partition_size, nullptr, 0, true, stream);
 }
 
 // device-visible address of a pool: device memory as is, pinned host memory

@@ -15,6 +15,12 @@
 // DPP and lane-rows are merged with shuffles at the end of the item.  Scores
 // are kept in log2 units so that v_exp_f32 computes the exponentials.
 //
+// An int8 cache (group-wise codes with one scale per token and KV head) is read
+// as biased codes (code + 128, see int8x16_biased): a token's score is
+// (q . (c + 128) - 128 sum q) * k_scale, and its value enters the accumulator
+// weighted by p * v_scale, with 128 times the sum of those weights taken off
+// once at the end of the item.
+//
 // A cut item (split context) writes its (max, sum, normalised output) to the
 // workspace and a reduction kernel below merges the pieces; an item that holds
 // a whole context writes the output directly.
@@ -84,8 +90,14 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
                 for (int i = 0; i < VEC; ++i) qf[i] *= a.qk_scale;
             }
             __builtin_amdgcn_s_waitcnt(0);
+            float qbias = 0.0f;                      // int8: 128 * this lane's sum of q
+            if constexpr (KVDT == PA_INT8) {
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) qbias += qf[i];
+                qbias *= 128.0f;
+            }
 
-            float m = kNegInf, l = 0.0f;
+            float m = kNegInf, l = 0.0f, wsum = 0.0f;   // wsum: int8, sum of p * v_scale
             float acc[VEC];
 #pragma unroll
             for (int i = 0; i < VEC; ++i) acc[i] = 0.0f;
@@ -110,6 +122,7 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
                 for (int c = ts; c < te; c += CH) {
                     Raw16 kr[U], vr[U];
                     bool valid[U];
+                    float kst[U], vst[U];                // int8: the tokens' scales
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int t = c + u * RPI + row;
@@ -122,17 +135,24 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
                         const int64_t byte_off = (r * D + col * VEC) * EB;
                         kr[u] = load16_stream(kbase + byte_off);
                         vr[u] = load16_stream(vbase + byte_off);
+                        if constexpr (KVDT == PA_INT8) {   // scale pools share the row index
+                            kst[u] = a.k_scales[r];
+                            vst[u] = a.v_scales[r];
+                        }
                     }
                     float sc[U];
                     float mc = kNegInf;
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         float kf[VEC];
-                        unpack16<KVDT>(kr[u], kf);
+                        if constexpr (KVDT == PA_INT8) int8x16_biased(kr[u], kf);
+                        else unpack16<KVDT>(kr[u], kf);
                         float dot = 0.0f;
 #pragma unroll
                         for (int i = 0; i < VEC; ++i) dot = __builtin_fmaf(qf[i], kf[i], dot);
+                        if constexpr (KVDT == PA_INT8) dot -= qbias;
                         dot = group_sum<LPR>(dot);
+                        if constexpr (KVDT == PA_INT8) dot *= kst[u];
                         sc[u] = valid[u] ? dot : kNegInf;
                         mc = fmaxf(mc, sc[u]);
                     }
@@ -140,15 +160,22 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
                     if (mn != kNegInf) {
                         const float alpha = fast_exp2(m - mn);
                         l *= alpha;
+                        if constexpr (KVDT == PA_INT8) wsum *= alpha;
 #pragma unroll
                         for (int i = 0; i < VEC; ++i) acc[i] *= alpha;
 #pragma unroll
                         for (int u = 0; u < U; ++u) {
                             if (valid[u]) {
-                                const float pu = fast_exp2(sc[u] - mn);
+                                float pu = fast_exp2(sc[u] - mn);
                                 l += pu;
                                 float vf[VEC];
-                                unpack16<KVDT>(vr[u], vf);
+                                if constexpr (KVDT == PA_INT8) {
+                                    pu *= vst[u];
+                                    wsum += pu;
+                                    int8x16_biased(vr[u], vf);
+                                } else {
+                                    unpack16<KVDT>(vr[u], vf);
+                                }
 #pragma unroll
                                 for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(pu, vf[i], acc[i]);
                             }
@@ -156,6 +183,10 @@ __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeArgs a) {
                         m = mn;
                     }
                 }
+            }
+            if constexpr (KVDT == PA_INT8) {
+#pragma unroll
+                for (int i = 0; i < VEC; ++i) acc[i] = __builtin_fmaf(-128.0f, wsum, acc[i]);
             }
 
             // merge the lane-rows of this wavefront (same column, disjoint tokens)
@@ -419,6 +450,12 @@ hipError_t launch_valu(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
             case PA_F32: return launch_dim<PA_FP8_E4M3, PA_F32>(a, head_dim, stream);
             case PA_F16: return launch_dim<PA_FP8_E4M3, PA_F16>(a, head_dim, stream);
             case PA_BF16: return launch_dim<PA_FP8_E4M3, PA_BF16>(a, head_dim, stream);
+        }
+    } else if (kv_dt == PA_INT8) {
+        switch (q_dt) {
+            case PA_F32: return launch_dim<PA_INT8, PA_F32>(a, head_dim, stream);
+            case PA_F16: return launch_dim<PA_INT8, PA_F16>(a, head_dim, stream);
+            case PA_BF16: return launch_dim<PA_INT8, PA_BF16>(a, head_dim, stream);
         }
     }
     return hipErrorInvalidValue;

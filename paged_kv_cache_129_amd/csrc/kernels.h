@@ -20,6 +20,8 @@ struct WriteArgs {
     int64_t num_slots;          // num_blocks * block_size
     float k_inv_scale;          // fp32 1/k_scale (fp8 pools)
     float v_inv_scale;
+    float* k_scales;            // int8 pools: scale pools [num_blocks][num_kv_heads][block_size]
+    float* v_scales;
 };
 hipError_t launch_kv_write(const WriteArgs& a, int src_dt, int kv_dt, hipStream_t stream);
 
@@ -83,6 +85,8 @@ struct DecodeArgs {
     const void* v_pool;
     const int32_t* tables;
     const int32_t* ctx_lens;
+    const float* k_scales;      // int8 cache: one scale per (block, kv head, slot)
+    const float* v_scales;
     float* ws;                  // partial records: m[nrec], l[nrec], o[nrec][head_dim]
     int64_t nrec;               // partial records in ws (set with the grid when balanced)
     int64_t rec_capacity;       // balanced: records ws can hold, or -1 (sized for any grid)

@@ -62,6 +62,65 @@ __global__ __launch_bounds__(256) void kv_write_kernel(WriteArgs a) {
     }
 }
 
+// int8 pools (group-wise): one wavefront per (token, KV head) quantises the head
+// vector on its own: amax over the vector (wavefront reduction), scale = amax / 127,
+// code = round-to-nearest-even(x / scale) clamped to [-127, 127] (codes 0 for a zero
+// vector), in float32 with correctly rounded divisions; lane 0 stores the scale.
+template <int SRC, int D>
+__global__ __launch_bounds__(256) void kv_write_int8_kernel(WriteArgs a) {
+    constexpr int PER = D / 64;                        // numbers per lane
+    const int lane = threadIdx.x & 63;
+    const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);   // (token, head) pair
+    const int64_t i = w / a.num_kv_heads;
+    if (i >= a.num_tokens) return;
+    const int64_t head = w - i * a.num_kv_heads;
+    const int64_t slot = a.slot_mapping[i];
+    if (slot < 0 || slot >= a.num_slots) return;
+    const int64_t blk = slot >> a.log2_bs;
+    const int64_t off = slot & ((1 << a.log2_bs) - 1);
+    const int64_t row = ((blk * a.num_kv_heads + head) << a.log2_bs) + off;   // scale index
+    const int64_t src = (i * a.num_kv_heads + head) * D + lane * PER;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv) {
+        const char* sp = reinterpret_cast<const char*>(kv ? a.v_new : a.k_new) + src * elem_bytes(SRC);
+        float x[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            if constexpr (SRC == PA_F32) x[k] = reinterpret_cast<const float*>(sp)[k];
+            else if constexpr (SRC == PA_F16) x[k] = (float)reinterpret_cast<const _Float16*>(sp)[k];
+            else x[k] = __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(sp)[k] << 16);
+        }
+        float amax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) amax = fmaxf(amax, fabsf(x[k]));
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+        const float scale = __fdiv_rn(amax, 127.0f);
+        uint32_t packed = 0;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            float q = scale > 0.0f ? __builtin_rintf(__fdiv_rn(x[k], scale)) : 0.0f;
+            q = fminf(fmaxf(q, -127.0f), 127.0f);
+            packed |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * k);
+        }
+        char* dp = reinterpret_cast<char*>(kv ? a.v_pool : a.k_pool) + row * D + lane * PER;
+        if constexpr (PER == 2) *reinterpret_cast<uint16_t*>(dp) = (uint16_t)packed;
+        else *reinterpret_cast<uint8_t*>(dp) = (uint8_t)packed;
+        if (lane == 0) (kv ? a.v_scales : a.k_scales)[row] = scale;
+    }
+}
+
+template <int SRC>
+hipError_t launch_int8(const WriteArgs& a, hipStream_t stream) {
+    const int64_t waves = (int64_t)a.num_tokens * a.num_kv_heads;
+    const int64_t blocks = (waves + 3) / 4;
+    if (a.head_dim == 64)
+        hipLaunchKernelGGL((kv_write_int8_kernel<SRC, 64>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((kv_write_int8_kernel<SRC, 128>), dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 template <int SRC, int KV>
 hipError_t launch(const WriteArgs& a, hipStream_t stream) {
     constexpr int VEC = 16 / elem_bytes(SRC);
@@ -86,6 +145,12 @@ hipError_t launch_kv_write(const WriteArgs& a, int src_dt, int kv_dt, hipStream_
             case PA_F32: return launch<PA_F32, PA_FP8_E4M3>(a, stream);
             case PA_F16: return launch<PA_F16, PA_FP8_E4M3>(a, stream);
             case PA_BF16: return launch<PA_BF16, PA_FP8_E4M3>(a, stream);
+        }
+    } else if (kv_dt == PA_INT8) {
+        switch (src_dt) {
+            case PA_F32: return launch_int8<PA_F32>(a, stream);
+            case PA_F16: return launch_int8<PA_F16>(a, stream);
+            case PA_BF16: return launch_int8<PA_BF16>(a, stream);
         }
     }
     return hipErrorInvalidValue;

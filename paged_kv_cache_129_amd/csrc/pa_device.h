@@ -14,7 +14,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
 __host__ __device__ constexpr int elem_bytes(int dt) {
-    return dt == PA_F32 ? 4 : (dt == PA_FP8_E4M3 ? 1 : 2);
+    return dt == PA_F32 ? 4 : ((dt == PA_FP8_E4M3 || dt == PA_INT8) ? 1 : 2);
 }
 
 // The fp8 path widens e4m3 codes through an fp16 bit pattern that carries
@@ -84,6 +84,7 @@ __device__ __forceinline__ void unpack16(const Raw16& r, float* f) {
             f[2 * i + 1] = __uint_as_float(r.w[i] & 0xFFFF0000u);
         }
     } else {   // e4m3 straight to fp32 (v_cvt_scalef32_pk_f32_fp8, same values)
+        static_assert(DT == PA_FP8_E4M3, "int8 codes go through int8x16_biased");
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.w[i], 1.0f / kFp8WidenFactor, false);
@@ -93,6 +94,19 @@ __device__ __forceinline__ void unpack16(const Raw16& r, float* f) {
             f[4 * i + 2] = hi[0];
             f[4 * i + 3] = hi[1];
         }
+    }
+}
+
+// 16 int8 codes -> the 16 floats code + 128, each in [1, 255] for codes in
+// [-127, 127].  Flipping the sign bits makes every byte the unsigned number
+// code + 128, which one v_cvt_f32_ubyteN converts exactly; the caller removes
+// the bias as 128 times the sum of the weights it applied.
+__device__ __forceinline__ void int8x16_biased(const Raw16& r, float* f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t u = r.w[i] ^ 0x80808080u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) f[4 * i + k] = (float)((u >> (8 * k)) & 0xFFu);
     }
 }
 

@@ -27,11 +27,14 @@ import numpy as np
 
 # ---------------------------------------------------------------- dtypes
 DTYPES = ("f32", "f16", "bf16", "fp8_e4m3")
-STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8_e4m3": np.uint8}
-ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
-# quiet-NaN bit patterns used to poison slots that hold no live token
-POISON_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F}
-_RAW = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8_e4m3": np.uint8}
+STORAGE = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16, "fp8_e4m3": np.uint8,
+           "int8": np.int8}
+ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1, "int8": 1}
+# quiet-NaN bit patterns used to poison slots that hold no live token (int8
+# codes: -128, which the group-wise codec never writes; its scale slots hold NaN)
+POISON_BITS = {"f32": 0x7FC00000, "f16": 0x7E00, "bf16": 0x7FC0, "fp8_e4m3": 0x7F, "int8": 0x80}
+_RAW = {"f32": np.uint32, "f16": np.uint16, "bf16": np.uint16, "fp8_e4m3": np.uint8,
+        "int8": np.uint8}
 
 
 def raw_view(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -182,6 +185,8 @@ class DecodeCase:
     k_scale: float = 1.0
     v_scale: float = 1.0
     partition_size: int = 0
+    k_scales: Optional[np.ndarray] = None   # int8 cache: float32 [NB, Hkv, bs] (pre-append)
+    v_scales: Optional[np.ndarray] = None
 
     @property
     def max_blocks(self) -> int:
@@ -271,6 +276,55 @@ def make_decode_case(name: str, config: str, *, num_seqs: int, num_heads: int, n
                       k_new=k_new, v_new=v_new, slot_mapping=slot_mapping, q=q,
                       scale=1.0 / math.sqrt(D), k_scale=k_scale, v_scale=v_scale,
                       partition_size=partition_size)
+
+
+def int8_storage(x: np.ndarray):
+    """Pre-existing contents of a group-wise int8 cache: fp32 head vectors
+    [..., D] -> (int8 codes, float32 scales [...]), one scale per vector set to
+    its amax / 127 and the codes made by torch's per-channel int8 quantiser
+    with those scales.  Like the fp8 cast above this only lays out inputs:
+    both implementations under test read the same bytes and scales."""
+    import torch
+    x = np.asarray(x, dtype=np.float32)
+    flat = x.reshape(-1, x.shape[-1])
+    if flat.shape[0] == 0:
+        return np.zeros(x.shape, np.int8), np.zeros(x.shape[:-1], np.float32)
+    amax = np.abs(flat).max(axis=1)
+    sc = (amax / np.float32(127)).astype(np.float32)
+    safe = np.where(sc > 0, sc, np.float32(1)).astype(np.float64)
+    tq = torch.quantize_per_channel(torch.from_numpy(flat), torch.from_numpy(safe),
+                                    torch.zeros(len(flat), dtype=torch.int64), 0, torch.qint8)
+    codes = np.maximum(tq.int_repr().numpy(), -127).astype(np.int8)
+    return codes.reshape(x.shape), sc.reshape(x.shape[:-1])
+
+
+def make_int8_case(name: str, config: str, *, num_seqs: int, num_heads: int, num_kv_heads: int,
+                   head_dim: int, block_size: int, context_lens: Sequence[int], q_dtype: str,
+                   num_blocks: Optional[int] = None, spare_blocks: int = 0, salt: int = 0,
+                   value_scale: float = 1.0) -> DecodeCase:
+    """A decode case over a group-wise int8 cache: the placement, lengths and
+    N(0,1) * value_scale draws of make_decode_case, pre-existing tokens stored as
+    int8 codes with a float32 scale per (token, KV head) (int8_storage); unused
+    slots hold code -128 and a NaN scale.  The new token's K/V stay in q_dtype
+    for the quantising cache write."""
+    base = make_decode_case(name, config, num_seqs=num_seqs, num_heads=num_heads,
+                            num_kv_heads=num_kv_heads, head_dim=head_dim, block_size=block_size,
+                            context_lens=context_lens, kv_dtype="f32", q_dtype=q_dtype,
+                            num_blocks=num_blocks, spare_blocks=spare_blocks, salt=salt,
+                            value_scale=value_scale)
+    NB, Hkv, bs, D = base.k_pool.shape
+    pools, scales = [], []
+    for src in (base.k_pool, base.v_pool):
+        pool = empty_pool(NB, Hkv, bs, D, "int8")
+        sc = np.full((NB, Hkv, bs), np.nan, dtype=np.float32)
+        live = ~np.isnan(src).any(axis=-1)              # slots holding a pre-existing token
+        codes, s = int8_storage(src[live])
+        pool[live] = codes
+        sc[live] = s
+        pools.append(pool)
+        scales.append(sc)
+    return dataclasses.replace(base, kv_dtype="int8", k_pool=pools[0], v_pool=pools[1],
+                               k_scales=scales[0], v_scales=scales[1])
 
 
 # ---------------------------------------------------------------- the five workloads
