@@ -21,7 +21,7 @@ LIB_NAME = "libpagedattn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 HIP_SOURCES = ["api.hip", "kv_write.hip", "copy_blocks.hip", "decode.hip", "decode_mfma.hip",
-               "prefill_mfma.hip"]
+               "prefill_mfma.hip", "decode_group.hip"]
 HOST_SOURCES = ["allocator.cpp"]
 ARCH = "gfx950"
 

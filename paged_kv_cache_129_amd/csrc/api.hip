@@ -59,11 +59,15 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Balanced split: partial records for two slots per (window, worker) and the
 // workers' range descriptors, for the most workers a launch can have on the
-// current device.
+// current device: per CU, kMaxWorkersPerCu one-head workers (per-head kernel),
+// or kMfmaMaxWorkersPerCu / kGroupMaxWorkersPerCu workers of unit_heads heads
+// (matrix-core kernels, groups of up to / beyond 16), whichever needs more.
 size_t balanced_record_bytes(int64_t num_seqs, int64_t unit_heads, int64_t head_dim) {
     const int64_t windows = (num_seqs + pa::kWindow - 1) / pa::kWindow;
-    const int64_t workers = (int64_t)pa::device_cus() * pa::kMaxWorkersPerCu;
-    return round256((size_t)(windows * workers * 2 * unit_heads) * (size_t)(head_dim + 2) * sizeof(float));
+    const int64_t per_cu = unit_heads > 16 ? pa::kGroupMaxWorkersPerCu : pa::kMfmaMaxWorkersPerCu;
+    const int64_t slots_per_cu = std::max<int64_t>((int64_t)pa::kMaxWorkersPerCu, per_cu * unit_heads);
+    const int64_t slots = (int64_t)pa::device_cus() * slots_per_cu;
+    return round256((size_t)(windows * slots * 2) * (size_t)(head_dim + 2) * sizeof(float));
 }
 size_t balanced_desc_bytes(int64_t num_seqs) {
     const int64_t windows = (num_seqs + pa::kWindow - 1) / pa::kWindow;
@@ -71,13 +75,13 @@ size_t balanced_desc_bytes(int64_t num_seqs) {
     return round256((size_t)(windows * workers) * pa::kDescWords * sizeof(int64_t));
 }
 
-// record slots per work unit: the matrix-core kernel's unit heads when it may
-// run (2 <= G <= kMaxGroup), else one head (per-head kernel); an upper bound
-// whichever kernel the data types select
+// record slots per work unit: all G query heads of a KV head when a
+// matrix-core kernel may run (2 <= G <= kMaxGroup), else one head (per-head
+// kernel); an upper bound whichever kernel the data types select
 int64_t unit_group(int32_t num_heads, int32_t num_kv_heads) {
     if (num_kv_heads <= 0 || num_heads % num_kv_heads != 0) return 1;
     const int g = num_heads / num_kv_heads;
-    return g >= 2 && g <= pa::kMaxGroup ? pa::mfma_unit_heads(g) : 1;
+    return g >= 2 && g <= pa::kMaxGroup ? g : 1;
 }
 
 }  // namespace

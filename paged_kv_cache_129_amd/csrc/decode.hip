@@ -299,10 +299,11 @@ __global__ __launch_bounds__(64) void lse_reduce_kernel(DecodeArgs a) {
 // past their end holds the last piece; its descriptor names the segment, and
 // the pieces are held by workers first..b (first: slot 1 unless its range
 // starts exactly at the segment, every other one: slot 0).  One wavefront per
-// worker: it reads the worker's descriptor and, if the worker holds such a
-// last piece, merges all heads of the segment's unit, 64 / (D / 16) heads per
-// pass with 16 consecutive dimensions of one head per lane (so every record
-// is fetched in 16-byte pieces, all records of a batch at once).
+// (worker, pass): it reads the worker's descriptor and, if the worker holds
+// such a last piece, merges its pass's share of the unit's heads, 64 / (D / 16)
+// heads with 16 consecutive dimensions of one head per lane (so every record
+// is fetched in 16-byte pieces, all records of a batch at once).  The passes of
+// a large unit run side by side instead of one after another.
 template <int QDT, int D>
 __global__ __launch_bounds__(256) void split_reduce_kernel(DecodeArgs a) {
     constexpr int LPH = D / 16;                 // lanes per head
@@ -310,30 +311,32 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(DecodeArgs a) {
     constexpr int B = 4;                        // records per batch
     const int64_t windows = (a.num_seqs + kWindow - 1) / kWindow;
     const int GR = a.unit_heads;                        // record slots per unit
+    const int NP = (GR + HP - 1) / HP;                  // passes per worker
     const int lane = threadIdx.x & 63;
     const int hl = lane / LPH, d0 = (lane % LPH) * 16;
-    const int64_t wb = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
-    if (wb >= windows * a.workers) return;
+    const int64_t wv = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6);
+    if (wv >= windows * a.workers * NP) return;
+    const int pass = (int)(wv % NP);
+    const int64_t wb = wv / NP;
     const int64_t win = wb / a.workers, b = wb % a.workers;
+    const int h0 = pass * HP;
     // The common case, a segment cut once that started inside worker b - 1's range, has
-    // its pieces in slot 1 of worker b - 1 and slot 0 of worker b: their records for
-    // the first SP passes are loaded together with the descriptor (in bounds whatever
-    // the descriptor says; used only in that case).
-    constexpr int SP = D == 64 ? 2 : 1;
-    float smv[SP][2], slv[SP][2];
-    float4 sov[SP][2][4];
-#pragma unroll
-    for (int p = 0; p < SP; ++p) {
-        const int isp = min(p * HP + hl, GR - 1);
+    // its pieces in slot 1 of worker b - 1 and slot 0 of worker b: their records are
+    // loaded together with the descriptor (in bounds whatever the descriptor says; used
+    // only in that case).
+    float smv[2], slv[2];
+    float4 sov[2][4];
+    {
+        const int isp = min(h0 + hl, GR - 1);
         const int64_t rs[2] = {((win * a.workers + (b > 0 ? b - 1 : b)) * 2 + 1) * GR + isp,
                                ((win * a.workers + b) * 2 + 0) * GR + isp};
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
-            smv[p][q] = a.ws[rs[q]];
-            slv[p][q] = a.ws[a.nrec + rs[q]];
+            smv[q] = a.ws[rs[q]];
+            slv[q] = a.ws[a.nrec + rs[q]];
             const float4* op = reinterpret_cast<const float4*>(a.ws + 2 * a.nrec + rs[q] * D + d0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) sov[p][q][v] = op[v];
+            for (int v = 0; v < 4; ++v) sov[q][v] = op[v];
         }
     }
     const int64_t* d = a.desc + wb * kDescWords;
@@ -349,70 +352,61 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(DecodeArgs a) {
     const int hg0 = (unit % a.units_per_kv) * GR;
     const int nh = min(GR, Gq - hg0);                   // heads of the unit
     const int64_t head0 = (int64_t)(unit / a.units_per_kv) * Gq + hg0;
-    for (int pass = 0; pass < (GR + HP - 1) / HP; ++pass) {
-        const int h0 = pass * HP;
-        if (h0 >= nh) break;
-        const int i = min(h0 + hl, nh - 1);             // lanes past the unit repeat its last head
-        auto rec = [&](int k) -> int64_t {
-            const int64_t w = first + k;
-            return ((win * a.workers + w) * 2 + (w * range >= start ? 0 : 1)) * GR + i;
-        };
-        float M = kNegInf, den = 0.0f, num[16];
+    if (h0 >= nh) return;
+    const int i = min(h0 + hl, nh - 1);                 // lanes past the unit repeat its last head
+    auto rec = [&](int k) -> int64_t {
+        const int64_t w = first + k;
+        return ((win * a.workers + w) * 2 + (w * range >= start ? 0 : 1)) * GR + i;
+    };
+    float M = kNegInf, den = 0.0f, num[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) num[e] = 0.0f;
-        // online merge of one piece's record (pieces in range order)
-        auto take = [&](float mq, float lq, const float4* oq) {
-            if (mq != kNegInf) {
-                const float Mn = fmaxf(M, mq);
-                const float sc = (M == kNegInf) ? 0.0f : fast_exp2(M - Mn);
-                const float w = fast_exp2(mq - Mn) * lq;
-                den = den * sc + w;
+    for (int e = 0; e < 16; ++e) num[e] = 0.0f;
+    // online merge of one piece's record (pieces in range order)
+    auto take = [&](float mq, float lq, const float4* oq) {
+        if (mq != kNegInf) {
+            const float Mn = fmaxf(M, mq);
+            const float sc = (M == kNegInf) ? 0.0f : fast_exp2(M - Mn);
+            const float w = fast_exp2(mq - Mn) * lq;
+            den = den * sc + w;
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    num[4 * v + 0] = num[4 * v + 0] * sc + w * oq[v].x;
-                    num[4 * v + 1] = num[4 * v + 1] * sc + w * oq[v].y;
-                    num[4 * v + 2] = num[4 * v + 2] * sc + w * oq[v].z;
-                    num[4 * v + 3] = num[4 * v + 3] * sc + w * oq[v].w;
-                }
-                M = Mn;
+            for (int v = 0; v < 4; ++v) {
+                num[4 * v + 0] = num[4 * v + 0] * sc + w * oq[v].x;
+                num[4 * v + 1] = num[4 * v + 1] * sc + w * oq[v].y;
+                num[4 * v + 2] = num[4 * v + 2] * sc + w * oq[v].z;
+                num[4 * v + 3] = num[4 * v + 3] * sc + w * oq[v].w;
             }
-        };
-        bool done = false;
-#pragma unroll
-        for (int p = 0; p < SP; ++p) {
-            if (p == pass && n == 2 && t0 < range) {    // the records loaded up front (a segment
+            M = Mn;
+        }
+    };
+    if (n == 2 && t0 < range) {                         // the records loaded up front (a segment
                                                         // starting a range keeps its slot 0 there)
-                take(smv[p][0], slv[p][0], sov[p][0]);
-                take(smv[p][1], slv[p][1], sov[p][1]);
-                done = true;
+        take(smv[0], slv[0], sov[0]);
+        take(smv[1], slv[1], sov[1]);
+    } else {
+        for (int k0 = 0; k0 < n; k0 += B) {
+            float mv[B], lv[B];
+            float4 ov[B][4];
+#pragma unroll
+            for (int q = 0; q < B; ++q) {
+                const int64_t r = rec(min(k0 + q, n - 1));
+                mv[q] = a.ws[r];
+                lv[q] = a.ws[a.nrec + r];
+                const float4* op = reinterpret_cast<const float4*>(a.ws + 2 * a.nrec + r * D + d0);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) ov[q][v] = op[v];
             }
+#pragma unroll
+            for (int q = 0; q < B; ++q)
+                if (k0 + q < n) take(mv[q], lv[q], ov[q]);
         }
-        if (!done) {
-            for (int k0 = 0; k0 < n; k0 += B) {
-                float mv[B], lv[B];
-                float4 ov[B][4];
+    }
+    if (h0 + hl < nh) {
+        const float f = den > 0.0f ? a.out_scale / den : 0.0f;
 #pragma unroll
-                for (int q = 0; q < B; ++q) {
-                    const int64_t r = rec(min(k0 + q, n - 1));
-                    mv[q] = a.ws[r];
-                    lv[q] = a.ws[a.nrec + r];
-                    const float4* op = reinterpret_cast<const float4*>(a.ws + 2 * a.nrec + r * D + d0);
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) ov[q][v] = op[v];
-                }
-#pragma unroll
-                for (int q = 0; q < B; ++q)
-                    if (k0 + q < n) take(mv[q], lv[q], ov[q]);
-            }
-        }
-        if (h0 + hl < nh) {
-            const float f = den > 0.0f ? a.out_scale / den : 0.0f;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) num[e] *= f;
-            char* op = reinterpret_cast<char*>(a.out) +
-                       (((int64_t)s * a.num_heads + head0 + i) * D + d0) * elem_bytes(QDT);
-            store_vals<QDT>(op, num, 16);
-        }
+        for (int e = 0; e < 16; ++e) num[e] *= f;
+        char* op = reinterpret_cast<char*>(a.out) +
+                   (((int64_t)s * a.num_heads + head0 + i) * D + d0) * elem_bytes(QDT);
+        store_vals<QDT>(op, num, 16);
     }
 }
 
@@ -464,7 +458,8 @@ hipError_t launch_valu(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
 template <int QDT>
 hipError_t launch_reduce(DecodeArgs& a, int head_dim, hipStream_t stream) {
     if (a.part_tokens < 0) {
-        const int64_t waves = (a.num_seqs + kWindow - 1) / kWindow * (int64_t)a.workers;
+        const int passes = (a.unit_heads + 64 / (head_dim / 16) - 1) / (64 / (head_dim / 16));
+        const int64_t waves = (a.num_seqs + kWindow - 1) / kWindow * (int64_t)a.workers * passes;
         auto k = head_dim == 64 ? split_reduce_kernel<QDT, 64> : split_reduce_kernel<QDT, 128>;
         hipLaunchKernelGGL(k, dim3((uint32_t)((waves + 3) / 4)), dim3(256), 0, stream, a);
         return hipGetLastError();
@@ -530,13 +525,14 @@ int device_cus() {
     return cus;
 }
 
-int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers, DecodeArgs& a) {
+int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers, DecodeArgs& a,
+                    int max_workers_per_cu) {
     a.units = units;
     a.simds = device_cus() * 4;                         // four SIMDs per compute unit
     const int per_wg = wave_workers ? threads / 64 : 1;
     int64_t grid;
     if (a.part_tokens < 0) {
-        grid = persistent_grid(kernel, threads, (int64_t)device_cus() * kMaxWorkersPerCu / per_wg);
+        grid = persistent_grid(kernel, threads, (int64_t)device_cus() * max_workers_per_cu / per_wg);
         const int64_t windows = (a.num_seqs + kWindow - 1) / kWindow;
         a.nrec = windows * grid * per_wg * 2 * a.unit_heads;
         if (a.rec_capacity >= 0 && a.nrec > a.rec_capacity) return -1;
@@ -551,7 +547,9 @@ hipError_t launch_decode(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                          hipStream_t stream) {
     const int group = a.num_heads / a.num_kv_heads;
     hipError_t e;
-    if (decode_mfma_supported(q_dt, kv_dt, head_dim, group))
+    if (decode_group_supported(q_dt, kv_dt, head_dim, group))
+        e = launch_decode_group(a, q_dt, kv_dt, head_dim, stream);
+    else if (decode_mfma_supported(q_dt, kv_dt, head_dim, group))
         e = launch_decode_mfma(a, q_dt, kv_dt, head_dim, stream);
     else
         e = launch_valu(a, q_dt, kv_dt, head_dim, stream);

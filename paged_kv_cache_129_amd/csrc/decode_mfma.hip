@@ -1,11 +1,10 @@
-// paged_attention_decode, matrix-core path for grouped heads (2 <= G <= 128
-// query heads per KV head).
+// paged_attention_decode, matrix-core path for grouped heads (2 <= G <= 16
+// query heads per KV head; larger groups: decode_group.hip).
 //
 // When several query heads share one KV head (KV 缓存与分页注意力 §11;
 // KV Cache从原理到实战 §5.3), one pass over a KV tile serves all G heads, and
 // scores = K·Q^T and out = P·V become small dense contractions on the matrix
-// cores: the heads (padded to 16, or cut into units of 16 or 32 for large
-// groups) are one MFMA dimension, 16 tokens another.
+// cores: the heads (padded to 16) are one MFMA dimension, 16 tokens another.
 //
 // Work items come from worklist.h; each wavefront is a worker that streams
 // its items in 16-token chunks.  Per chunk it
@@ -285,45 +284,82 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
                         for (int i = 0; i < 4; ++i) live[i] = row_of(c0 + 4 * j + i) >= 0;
                     }
 
-                    // ---- per tile: scores S^T[token][head], online softmax per head column
+                    // ---- scores S^T[token][head] of every tile (the matrix cores work on
+                    // them while the vector units go on)
+                    f32x4 sc[TILES];
+#pragma unroll
+                    for (int tt = 0; tt < TILES; ++tt) {
+                        sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int c = 0; c < NC; ++c) sc[tt] = mma32<MT>(kop[c], qop[tt][c], sc[tt]);
+                    }
+                    // ---- online softmax per head column.  The reference maximum moves
+                    // only when a score passes it by more than kMaxSlack (weights then stay
+                    // below 2^kMaxSlack); a lane's own scores tell whether that can happen,
+                    // and only then (rarely, after the first chunks) are column maxima taken
+                    // across the column's four lanes and the accumulators rescaled.
+                    // With every token present and a positive scale the scaled maximum is
+                    // the maximum scaled, and no masks are needed.
+                    const bool fast = full && a.qk_scale > 0.0f;
+                    float lm[TILES];
+                    if (fast) {
+#pragma unroll
+                        for (int tt = 0; tt < TILES; ++tt)
+                            lm[tt] = fmaxf(fmaxf(sc[tt][0], sc[tt][1]), fmaxf(sc[tt][2], sc[tt][3])) * a.qk_scale;
+                    } else {
+#pragma unroll
+                        for (int tt = 0; tt < TILES; ++tt) {
+                            float mx = kNegInf;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) mx = fmaxf(mx, live[i] ? sc[tt][i] * a.qk_scale : kNegInf);
+                            lm[tt] = mx;
+                        }
+                    }
+                    bool grow = false;
+#pragma unroll
+                    for (int tt = 0; tt < TILES; ++tt) grow = grow || lm[tt] > m[tt] + kMaxSlack;
+                    if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+                        for (int tt = 0; tt < TILES; ++tt) {
+                            const float mx = max_over_groups(lm[tt]);
+                            const float mn = (mx > m[tt] + kMaxSlack) ? mx : m[tt];
+                            // (moving from -inf gives exp2(-inf) = 0)
+                            const float alpha = mn != m[tt] ? fast_exp2(m[tt] - mn) : 1.0f;
+                            if (__builtin_amdgcn_ballot_w64(mn != m[tt])) {
+#pragma unroll
+                                for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] *= alpha;
+                                l[tt] *= alpha;
+                            }
+                            m[tt] = mn;
+                        }
+                    }
+                    // ---- weights -> MFMA operands; the running sum adds the weights as
+                    // the matrix cores see them (fp16: the rounded values, two per dot
+                    // instruction; bf16: a high and a low part that together keep ~16 bits)
                     Op4 pop[TILES], plo[TILES];
 #pragma unroll
                     for (int tt = 0; tt < TILES; ++tt) {
-                        if (tt > 0 && 16 * tt >= nh) break;      // a tile with no heads of the unit
-                        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                        for (int c = 0; c < NC; ++c) sc = mma32<MT>(kop[c], qop[tt][c], sc);
-                        float sv[4];
-                        float mx = kNegInf;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            sv[i] = live[i] ? sc[i] * a.qk_scale : kNegInf;
-                            mx = fmaxf(mx, sv[i]);
-                        }
-                        mx = max_over_groups(mx);
-                        // the reference maximum moves only when a score passes it by more
-                        // than kMaxSlack (weights then stay below 2^kMaxSlack), so the
-                        // accumulators are rarely rescaled
-                        const float mn = (mx > m[tt] + kMaxSlack) ? mx : m[tt];
-                        const bool moved = mn != m[tt];
-                        // (moving from -inf gives exp2(-inf) = 0)
-                        const float alpha = moved ? fast_exp2(m[tt] - mn) : 1.0f;
                         float pr[4];
-                        float psum = 0.0f;
+                        const float mn = m[tt];
+                        if (fast) {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            pr[i] = live[i] ? fast_exp2(sv[i] - mn) : 0.0f;
-                            psum += pr[i];
-                        }
-                        l[tt] = l[tt] * alpha + psum;
-                        m[tt] = mn;
-                        if (__builtin_amdgcn_ballot_w64(moved)) {
+                            for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(sc[tt][i], a.qk_scale, -mn));
+                        } else {
 #pragma unroll
-                            for (int dt = 0; dt < NDT; ++dt) acc[tt][dt] *= alpha;
+                            for (int i = 0; i < 4; ++i)
+                                pr[i] = live[i] ? fast_exp2(fmaf(sc[tt][i], a.qk_scale, -mn)) : 0.0f;
                         }
                         pop[tt].w[0] = pack2<MT>(pr[0], pr[1]);
                         pop[tt].w[1] = pack2<MT>(pr[2], pr[3]);
-                        if constexpr (MT == PA_BF16) {
+                        if constexpr (MT == PA_F16) {
+                            float lt = l[tt];
+#pragma unroll
+                            for (int q = 0; q < 2; ++q)
+                                lt = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pop[tt].w[q]),
+                                                            half2_t{(_Float16)1.0f, (_Float16)1.0f}, lt, false);
+                            l[tt] = lt;
+                        } else {
+                            l[tt] += (pr[0] + pr[1]) + (pr[2] + pr[3]);
 #pragma unroll
                             for (int q = 0; q < 2; ++q) {
                                 const float h0 = __uint_as_float(pop[tt].w[q] << 16);
@@ -371,7 +407,6 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
                         const Op4 vop = read_tr16(vs + (4 * j + (c16 >> 2)) * LDV + 16 * dt + 4 * (c16 & 3));
 #pragma unroll
                         for (int tt = 0; tt < TILES; ++tt) {
-                            if (tt > 0 && 16 * tt >= nh) break;
                             acc[tt][dt] = mma16<MT>(vop, pop[tt], acc[tt][dt]);
                             if constexpr (MT == PA_BF16) acc[tt][dt] = mma16<MT>(vop, plo[tt], acc[tt][dt]);
                         }
@@ -434,30 +469,21 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
     }
 }
 
-template <int KVDT, int QDT, int D, int TILES>
-hipError_t launch_tiles(DecodeArgs& a, hipStream_t stream) {
+template <int KVDT, int QDT, int D>
+hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
     constexpr int NW = 4;
-    constexpr int PD = TILES == 1 ? 3 : 2;   // chunks in flight per wavefront (measured best)
+    constexpr int TILES = 1;
+    constexpr int PD = 3;                    // chunks in flight per wavefront (measured best)
     auto kernel = a.log2_bs >= 4 ? decode_mfma_kernel<KVDT, QDT, D, NW, TILES, PD, true>
                                  : decode_mfma_kernel<KVDT, QDT, D, NW, TILES, PD, false>;
-    const int G = a.num_heads / a.num_kv_heads;
-    a.unit_heads = G <= 16 ? G : 16 * TILES;
+    a.unit_heads = a.num_heads / a.num_kv_heads;        // a unit: every query head of a KV head
+    a.units_per_kv = 1;
     a.seg_cost = 64;                                    // an item start, in tokens (measured)
-    a.units_per_kv = (G + a.unit_heads - 1) / a.unit_heads;
     const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), NW * 64,
-                                     a.num_kv_heads * a.units_per_kv, 1, a);
+                                     a.num_kv_heads, 1, a, kMfmaMaxWorkersPerCu);
     if (grid < 0) return hipErrorOutOfMemory;
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(NW * 64), 0, stream, a);
     return hipGetLastError();
-}
-
-template <int KVDT, int QDT, int D>
-hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
-    switch (mfma_tiles(a.num_heads / a.num_kv_heads)) {
-        case 1: return launch_tiles<KVDT, QDT, D, 1>(a, stream);
-        case 2: return launch_tiles<KVDT, QDT, D, 2>(a, stream);
-    }
-    return hipErrorInvalidValue;
 }
 
 template <int KVDT, int QDT>
@@ -470,7 +496,7 @@ hipError_t launch_dim(DecodeArgs& a, int head_dim, hipStream_t stream) {
 }  // namespace
 
 bool decode_mfma_supported(int q_dt, int kv_dt, int head_dim, int group) {
-    if (group < 2 || group > kMaxGroup) return false;
+    if (group < 2 || group > 16) return false;
     if (head_dim != 64 && head_dim != 128) return false;
     if (q_dt != PA_F16 && q_dt != PA_BF16) return false;
     return kv_dt == q_dt || kv_dt == PA_FP8_E4M3;

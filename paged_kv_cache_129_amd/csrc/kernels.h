@@ -61,22 +61,16 @@ constexpr int kDescWords = 6;
 // 32 wavefronts per CU at most, each a worker
 constexpr int kMaxWorkersPerCu = 32;
 
-// Matrix-core kernel: a wavefront computes one or two 16-head tiles of one KV
-// head's query heads from one read of K and V; larger groups are split into
-// units of equal tile counts (whose reads of the same K and V mostly meet in
-// L2).  Measured on Falcon-7B's 71 heads: two tiles per wavefront beat one
-// (five reads) and three to five (one or two wavefronts per SIMD leave the
-// dependent matrix-core and softmax steps exposed).
+// Matrix-core kernels.  Up to 16 query heads per KV head, a wavefront computes
+// one 16-head tile of a KV head's query heads (decode_mfma.hip); larger groups
+// (multi-query attention among them) take a workgroup per KV head, one
+// wavefront per 16-head tile, sharing one load and conversion of K and V
+// (decode_group.hip).  Either way a work unit is every query head of a KV head.
 constexpr int kMaxGroup = 128;
-__host__ __device__ constexpr int mfma_tiles(int group) {
-    const int tiles = (group + 15) / 16;
-    const int units = (tiles + 1) / 2;
-    return (tiles + units - 1) / units;
-}
-// query heads per work unit (record slots per unit) of the matrix-core kernel
-__host__ __device__ constexpr int mfma_unit_heads(int group) {
-    return group <= 16 ? group : 16 * mfma_tiles(group);
-}
+// workers per CU of a launch at most: wavefronts (per-tile kernel), workgroups
+// (group kernel)
+constexpr int kMfmaMaxWorkersPerCu = 8;
+constexpr int kGroupMaxWorkersPerCu = 4;
 
 struct DecodeArgs {
     const void* q;
@@ -120,7 +114,8 @@ int device_cus();
 // workgroups; records the worker count (and, when balanced, the partial-record
 // count) in `a`.  Returns -1 when the balanced records would not fit
 // a.rec_capacity (the launcher then returns hipErrorOutOfMemory unlaunched).
-int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers, DecodeArgs& a);
+int64_t decode_grid(const void* kernel, int threads, int units, int wave_workers, DecodeArgs& a,
+                    int max_workers_per_cu = kMaxWorkersPerCu);
 hipError_t launch_decode(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                          hipStream_t stream);
 
@@ -150,10 +145,14 @@ struct PrefillArgs {
 bool prefill_supported(int q_dt, int kv_dt, int head_dim);
 hipError_t launch_prefill(PrefillArgs& a, int q_dt, int kv_dt, int head_dim, hipStream_t stream);
 
-// matrix-core kernel for grouped heads, 2 <= G <= kMaxGroup (decode_mfma.hip)
+// matrix-core kernel for grouped heads, 2 <= G <= 16 (decode_mfma.hip)
 bool decode_mfma_supported(int q_dt, int kv_dt, int head_dim, int group);
 hipError_t launch_decode_mfma(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                               hipStream_t stream);
+// matrix-core kernel for large groups, 16 < G <= kMaxGroup (decode_group.hip)
+bool decode_group_supported(int q_dt, int kv_dt, int head_dim, int group);
+hipError_t launch_decode_group(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
+                               hipStream_t stream);
 
 
 

@@ -103,19 +103,21 @@ def test_workspace_size():
     assert ws(4, 8, 8, 128, 512, 512) == 0
     # split-context: (max, sum, output) per (sequence, head, partition)
     assert ws(4, 8, 8, 128, 1025, 512) == r256(4 * 8 * 3 * 130 * 4)
-    # balanced: two records of a work unit's heads per worker, at most 32 workers
-    # (wavefronts) per CU (MI355X: 256 CUs, also the fallback without a device),
-    # then one 6-word range descriptor per worker; all per started window of 1024
-    # sequences.  A unit holds all G query heads of a KV head up to G = 16, else
-    # one or two whole 16-head tiles (equal counts per unit).
+    # balanced: two records per worker for each head of a work unit, then one
+    # 6-word range descriptor per worker (at most 32 workers per CU), all per
+    # started window of 1024 sequences (MI355X: 256 CUs, also the fallback
+    # without a device).  A unit is one head (per-head kernel, up to 32 workers
+    # per CU) or, for 2 <= G <= 128, all G heads of a KV head (matrix-core
+    # kernels: up to 8 workers per CU for G <= 16, 4 beyond); the records are
+    # sized for whichever needs more.
     cus = 256
-    for S, H, Hkv, D, unit in ((4, 8, 2, 128, 4), (4, 32, 32, 64, 1), (1500, 71, 1, 64, 32),
-                               (4, 128, 1, 64, 32), (4, 100, 1, 128, 32), (4, 20, 1, 128, 32),
-                               (4, 48, 1, 64, 32), (4, 17, 1, 64, 32)):
+    for S, H, Hkv, D, G in ((4, 8, 2, 128, 4), (4, 32, 32, 64, 1), (1500, 71, 1, 64, 71),
+                            (4, 128, 1, 64, 128), (4, 100, 1, 128, 100), (4, 20, 1, 128, 20),
+                            (4, 48, 1, 64, 48), (4, 17, 1, 64, 17), (4, 64, 8, 128, 8)):
         windows = (S + 1023) // 1024
-        workers = cus * 32
-        expect = r256(windows * workers * 2 * unit * (D + 2) * 4) + \
-            r256(windows * workers * 6 * 8)
+        slots_per_cu = max(32, (4 if G > 16 else 8) * G) if G >= 2 else 32
+        expect = r256(windows * cus * slots_per_cu * 2 * (D + 2) * 4) + \
+            r256(windows * cus * 32 * 6 * 8)
         assert ws(S, H, Hkv, D, 100, -1) == expect, (S, H, Hkv, D)
     assert ws(0, 8, 8, 128, 100, 0) == 0
     assert ws(4, 8, 8, 128, 100, -2) == 0
