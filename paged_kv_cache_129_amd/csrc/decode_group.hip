@@ -81,11 +81,22 @@ void decode_group_kernel(DecodeArgs a) {
     for (int s0 = 0; s0 < a.num_seqs; s0 += kWindow) {
         sch.build(a, s0, min(kWindow, a.num_seqs - s0), a.units, wl_lds, (int)blockIdx.x,
                   (int)gridDim.x, tid == 0);
+        // The first block-table slice of the next item is loaded while the current
+        // item streams, so that starting an item costs one memory round trip (its
+        // first K/V chunks) instead of two.
+        TablePrefetch<kGThreads, kGTable> tpre;
+        auto prefetch = [&](const Item& it) {
+            tpre.issue(a.tables + (int64_t)it.s * a.max_blocks, it.t0 >> a.log2_bs,
+                       table_span(a, it.t0, it.t1, kGTable), a.max_blocks, tid);
+        };
         Item itm;
-        while (sch.next(a, itm)) {
-            const int s = itm.s;
-            const int kvh = itm.unit;                            // one unit per KV head
-            const int t0 = itm.t0, t1 = itm.t1;
+        bool have = sch.next(a, itm);
+        if (have) prefetch(itm);
+        while (have) {
+            const Item cur = itm;
+            const int s = cur.s;
+            const int kvh = cur.unit;                            // one unit per KV head
+            const int t0 = cur.t0, t1 = cur.t1;
             const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
             const int hu = 16 * wave + c16;                      // this lane's head column
             const bool hlive = hu < G;
@@ -120,14 +131,21 @@ void decode_group_kernel(DecodeArgs a) {
 
             const int b_first = t0 >> a.log2_bs;
             const int b_end = (t1 + bs - 1) >> a.log2_bs;
+            __syncthreads();                                     // the previous item's table is read
+            tpre.store(tbl, min(b_end, b_first + kGTable) - b_first, a.num_blocks, tid);
+            __syncthreads();
+            have = sch.next(a, itm);
+            if (have) prefetch(itm);
             for (int sb = b_first; sb < b_end; sb += kGTable) {
                 const int se = min(b_end, sb + kGTable);
-                __syncthreads();                                 // the previous segment's table is read
-                for (int i = tid; i < se - sb; i += kGThreads) {
-                    const int b = trow[sb + i];
-                    tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
+                if (sb != b_first) {                             // later slices of a long item
+                    __syncthreads();
+                    for (int i = tid; i < se - sb; i += kGThreads) {
+                        const int b = trow[sb + i];
+                        tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
+                    }
+                    __syncthreads();
                 }
-                __syncthreads();
                 const int ts = max(t0, sb << a.log2_bs);
                 const int te = min(t1, se << a.log2_bs);
                 const int nch = (te - ts + kGChunk - 1) / kGChunk;
@@ -306,15 +324,15 @@ void decode_group_kernel(DecodeArgs a) {
                 if (hlive) {
                     const int head = kvh * G + hu;
                     const float inv_l = lt > 0.0f ? 1.0f / lt : 0.0f;
-                    const int64_t r = itm.rec0 + (int64_t)hu * itm.rec_stride;
-                    if (!itm.whole && j == 0) {
+                    const int64_t r = cur.rec0 + (int64_t)hu * cur.rec_stride;
+                    if (!cur.whole && j == 0) {
                         a.ws[r] = m;
                         a.ws[a.nrec + r] = lt;
                     }
 #pragma unroll
                     for (int dt = 0; dt < NDT; ++dt) {
                         const int d = 16 * dt + 4 * j;
-                        if (itm.whole) {
+                        if (cur.whole) {
                             const float f = inv_l * a.out_scale;
                             char* op = reinterpret_cast<char*>(a.out) +
                                        (((int64_t)s * a.num_heads + head) * D + d) * elem_bytes(QDT);
@@ -345,7 +363,7 @@ hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
     auto kernel = decode_group_kernel<KVDT, QDT, D, KT, NS, MINB>;
     a.unit_heads = a.num_heads / a.num_kv_heads;        // a unit: every query head of a KV head
     a.units_per_kv = 1;
-    a.seg_cost = 64;                                    // an item start, in tokens
+    a.seg_cost = 256;                                   // an item start, in tokens (measured)
     const int64_t grid = decode_grid(reinterpret_cast<const void*>(kernel), kGThreads,
                                      a.num_kv_heads, 0, a, kGroupMaxWorkersPerCu);
     if (grid < 0) return hipErrorOutOfMemory;
