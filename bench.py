@@ -171,7 +171,7 @@ def cpu_cores():
     return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
+ELEM = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1, "int8": 1}
 
 
 def raw_np(t):
@@ -315,6 +315,60 @@ class Llama70B(HostLayers):
         self.finish(pa, torch, partition_size, self.ctx.max())
 
 
+class Llama7BInt8(HostLayers):
+    """Llama-2-7B-shaped layer with a group-wise int8 cache (32 heads x 128, block
+    16, one float32 scale per token and KV head for K and for V), fp16 q/out:
+    16 sequences at context 2048, 8 layers in their own memory."""
+    name = "llama2-7b-shaped decode step, int8 KV (group-wise scales)"
+
+    def __init__(self, pa, W, torch, partition_size, args):
+        case = W.make_int8_case("llama7b_int8", "llama7b", num_seqs=16, num_heads=32,
+                                num_kv_heads=32, head_dim=128, block_size=16,
+                                context_lens=[2048] * 16, q_dtype="f16", spare_blocks=16)
+        self.place(torch, case, args.layers or 8)
+        ks = torch.from_numpy(case.k_scales).cuda()
+        vs = torch.from_numpy(case.v_scales).cuda()
+        for i, d in enumerate(self.layers):
+            d["k_scales"] = ks if i == 0 else ks.clone()
+            d["v_scales"] = vs if i == 0 else vs.clone()
+        torch.cuda.synchronize()
+        self.ctx_desc = "all 2048"
+        tokens = int(self.ctx.sum())
+        # codes once, plus each token's K and V scale per KV head
+        self.attn_bytes = attention_bytes(self.ctx, self.S, self.H, self.Hkv, self.D, 1, 2, self.bs) + \
+            tokens * 2 * self.Hkv * 4
+        self.write_bytes = write_bytes(self.S, self.Hkv, self.D, 2, 1) + self.S * 2 * self.Hkv * 4
+        self.finish(pa, torch, partition_size, self.ctx.max())
+
+    def decode(self, l):
+        d = self.layers[l]
+        self.pa.paged_attention_decode_int8(d["out"], d["q"], d["k_pool"], d["v_pool"],
+                                            d["k_scales"], d["v_scales"], self.tables, self.ctx_t,
+                                            max_context_len=self.max_ctx, scale=self.scale,
+                                            partition_size=self.partition_size, workspace=self.ws)
+
+    def step(self):
+        for l in range(self.L):
+            d = self.layers[l]
+            self.pa.kv_cache_write_int8(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"],
+                                        d["k_scales"], d["v_scales"], self.slots)
+            self.decode(l)
+
+    def cpu_inputs(self, l, s):
+        x = super().cpu_inputs(l, s)
+        d = self.layers[l]
+        nblk = x["local"].shape[1]
+        idx = self.torch.from_numpy(self._tables_np[s, :nblk].astype(np.int64)).cuda()
+        x["ks"], x["vs"] = d["k_scales"][idx].cpu().numpy(), d["v_scales"][idx].cpu().numpy()
+        return x
+
+    def cpu_run(self, oracle, x):
+        oracle.kv_write_int8(x["kp"], x["vp"], x["ks"], x["vs"], x["kn"], x["vn"], self.q_dtype,
+                             x["slot"], self.bs)
+        oracle.paged_attention(x["q"], self.q_dtype, x["kp"], x["vp"], "int8", x["local"],
+                               [x["n"]], self.bs, self.scale, x["ks"], x["vs"])
+
+
 class Tiny(HostLayers):
     """The tiny fp32 case: 4 sequences, contexts {5,10,3,16}, 2 heads of 64, block 4."""
     name = "tiny fp32 decode step, 1 layer"
@@ -453,10 +507,10 @@ class Llama7BPrefill(Workload):
 # launch configuration per workload: the fastest measured on MI355X (uniform
 # long contexts: one pass per (sequence, head); ragged batches: balanced split)
 DEFAULT_PARTITION = {"llama7b": 0, "opt13b": -1, "falcon7b": -1, "llama70b": -1, "tiny": 0,
-                     "llama7b_prefill": 0}
+                     "llama7b_prefill": 0, "llama7b_int8": 0}
 
 WORKLOADS = {"llama7b": Llama7B, "opt13b": Opt13B, "falcon7b": Falcon7B, "llama70b": Llama70B,
-             "tiny": Tiny, "llama7b_prefill": Llama7BPrefill}
+             "tiny": Tiny, "llama7b_prefill": Llama7BPrefill, "llama7b_int8": Llama7BInt8}
 
 
 def read_traffic(workload, partition_size, block_size):
@@ -737,7 +791,7 @@ def config_entry(key, wl, torch, oracle, args, cpu_seconds, cores):
 # every configuration of the workload set, measured after the headline one
 CONFIG_SET = [("tiny", {}), ("opt13b", {}), ("llama70b", {}), ("falcon7b", {"block_size": 8}),
               ("falcon7b", {"block_size": 16}), ("falcon7b", {"block_size": 32}),
-              ("falcon7b", {"block_size": 64}), ("llama7b_prefill", {})]
+              ("falcon7b", {"block_size": 64}), ("llama7b_prefill", {}), ("llama7b_int8", {})]
 
 
 def main():

@@ -24,8 +24,8 @@
 // One barrier per step separates the tile being read from the one being
 // written.  Work is shared out by worklist.h with workgroups as workers; a
 // worker's pieces of a cut context go to partial records that the reduction
-// kernels merge.  An fp8 cache is widened to fp16 (value * 2^-8; the factor is
-// folded into the scales).
+// kernels merge.  An fp8 cache is widened exactly to the query's type, fp16 or
+// bf16 (value * 2^-8; the factor is folded into the scales).
 #include "kernels.h"
 #include "mfma_util.h"
 #include "pa_device.h"
@@ -46,7 +46,9 @@ template <int KVDT, int QDT, int D, int KT, int NS, int MINB>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(MINB * kGWaves / 4)))
 void decode_group_kernel(DecodeArgs a) {
     constexpr int kGChunk = KT;
-    constexpr int MT = (KVDT == PA_FP8_E4M3) ? PA_F16 : KVDT;   // MFMA operand type
+    // MFMA operand type: the cache's, or for an fp8 cache the query's (e4m3 widens
+    // exactly to fp16 and to bf16, and a bf16 query keeps its range)
+    constexpr int MT = (KVDT == PA_FP8_E4M3) ? QDT : KVDT;
     constexpr int EB = elem_bytes(KVDT);
     constexpr int RB = D * EB;                                   // bytes of a cached row
     constexpr int PPR = RB / 16;                                 // 16-byte pieces per row
@@ -109,17 +111,11 @@ void decode_group_kernel(DecodeArgs a) {
                                        elem_bytes(QDT);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
+                    static_assert(QDT == MT, "the query is an MFMA operand as it is");
                     const Raw16 r = load16(qrow + (32 * c + 8 * j) * elem_bytes(QDT));
                     Op8 o;
-                    if constexpr (QDT == MT) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) o.w[q] = hlive ? r.w[q] : 0u;
-                    } else {                   // bf16 query with an fp16 MFMA: widen then round
-                        float f[8];
-                        unpack16<QDT>(r, f);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) o.w[q] = hlive ? pack_f16(f[2 * q], f[2 * q + 1]) : 0u;
-                    }
+                    for (int q = 0; q < 4; ++q) o.w[q] = hlive ? r.w[q] : 0u;
                     qop[c] = o;
                 }
             }
@@ -187,7 +183,7 @@ void decode_group_kernel(DecodeArgs a) {
                             if constexpr (KVDT == PA_FP8_E4M3) {
                                 uint32_t w[8];
 #pragma unroll
-                                for (int q = 0; q < 4; ++q) e4m3x4_to_f16x4(st.r[k].w[q], w[2 * q], w[2 * q + 1]);
+                                for (int q = 0; q < 4; ++q) e4m3x4_widen<MT>(st.r[k].w[q], w[2 * q], w[2 * q + 1]);
 #pragma unroll
                                 for (int q = 0; q < 8; ++q) w[q] = st.ok[k] ? w[q] : 0u;
                                 *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);

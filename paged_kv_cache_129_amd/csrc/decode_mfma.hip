@@ -24,8 +24,9 @@
 // With blocks of 16 tokens or more a chunk lies in one block: its pool offset
 // is wavefront-uniform (one table lookup per chunk) and each lane adds a fixed
 // offset; smaller blocks take a per-token lookup.  The next chunk's loads are
-// issued before the current one is computed.  An fp8 cache is widened to fp16
-// in registers (value * 2^-8; the factor is folded into the scales).
+// issued before the current one is computed.  An fp8 cache is widened exactly
+// to the query's type, fp16 or bf16, in registers (value * 2^-8; the factor is
+// folded into the scales).
 #include "kernels.h"
 #include "pa_device.h"
 #include "worklist.h"
@@ -55,7 +56,9 @@ __device__ __forceinline__ int dmap(int c, int j) {
 // and the younger one finishes its equal share well after it.
 template <int KVDT, int QDT, int D, int NW, int TILES, int PD, bool BIGB>
 __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
-    constexpr int MT = (KVDT == PA_FP8_E4M3) ? PA_F16 : KVDT;   // MFMA operand type
+    // MFMA operand type: the cache's, or for an fp8 cache the query's (e4m3 widens
+    // exactly to fp16 and to bf16, and a bf16 query keeps its range)
+    constexpr int MT = (KVDT == PA_FP8_E4M3) ? QDT : KVDT;
     constexpr int EB = elem_bytes(KVDT);
     constexpr int NC = D / 32;               // score MFMAs per chunk and tile
     constexpr int NDT = D / 16;              // output d-tiles
@@ -138,16 +141,10 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
                 const bool live = 16 * tt + c16 < nh;
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
+                    static_assert(QDT == MT, "the query is an MFMA operand as it is");
                     Op8 o;
-                    if constexpr (QDT == MT) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) o.w[q] = live ? pre.q[tt][c].w[q] : 0u;
-                    } else {                       // bf16 query with an fp16 MFMA: widen then round
-                        float f[8];
-                        unpack16<QDT>(pre.q[tt][c], f);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) o.w[q] = live ? pack_f16(f[2 * q], f[2 * q + 1]) : 0u;
-                    }
+                    for (int q = 0; q < 4; ++q) o.w[q] = live ? pre.q[tt][c].w[q] : 0u;
                     qop[tt][c] = o;
                 }
             }
@@ -263,8 +260,8 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
                     for (int c = 0; c < NC; ++c) {
                         if constexpr (KVDT == PA_FP8_E4M3) {
-                            e4m3x4_to_f16x4(R.k[c].w[0], kop[c].w[0], kop[c].w[1]);
-                            e4m3x4_to_f16x4(R.k[c].w[2], kop[c].w[2], kop[c].w[3]);
+                            e4m3x4_widen<MT>(R.k[c].w[0], kop[c].w[0], kop[c].w[1]);
+                            e4m3x4_widen<MT>(R.k[c].w[2], kop[c].w[2], kop[c].w[3]);
                         } else {
                             kop[c] = R.k[c];
                         }
@@ -382,7 +379,7 @@ __global__ __launch_bounds__(NW * 64, 1) void decode_mfma_kernel(DecodeArgs a) {
                         if constexpr (KVDT == PA_FP8_E4M3) {
                             uint32_t wv[8];
 #pragma unroll
-                            for (int q = 0; q < 4; ++q) e4m3x4_to_f16x4(R.v[u].w[q], wv[2 * q], wv[2 * q + 1]);
+                            for (int q = 0; q < 4; ++q) e4m3x4_widen<MT>(R.v[u].w[q], wv[2 * q], wv[2 * q + 1]);
                             if (!full) {
 #pragma unroll
                                 for (int q = 0; q < 8; ++q) wv[q] = R.vlive[u] ? wv[q] : 0u;

@@ -61,6 +61,21 @@ __device__ __forceinline__ void e4m3x4_to_f16x4(uint32_t w, uint32_t& lo, uint32
     hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f / kFp8WidenFactor, true));
 }
 
+// The same widening to bf16 (v_cvt_scalef32_pk_bf16_fp8, scale 2^-8): bf16 has
+// more significant bits than e4m3 and a wider exponent range, so this is
+// exact too.  Used when the query is bf16, whose range fp16 cannot hold.
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f / kFp8WidenFactor, false));
+    hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f / kFp8WidenFactor, true));
+}
+
+// e4m3 codes widened to the matrix-core operand type MT (fp16 or bf16)
+template <int MT>
+__device__ __forceinline__ void e4m3x4_widen(uint32_t w, uint32_t& lo, uint32_t& hi) {
+    if constexpr (MT == PA_BF16) e4m3x4_to_bf16x4(w, lo, hi);
+    else e4m3x4_to_f16x4(w, lo, hi);
+}
+
 __device__ __forceinline__ void f16x2_to_f32(uint32_t w, float& a, float& b) {
     const half2_t h = __builtin_bit_cast(half2_t, w);
     a = (float)h.x;

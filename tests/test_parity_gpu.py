@@ -2,6 +2,7 @@
 seeded inputs.  Cache writes and block copies must be bit-exact; attention
 must be within max-abs 1e-4 (fp32 cache), 5e-3 (fp16/bf16) or 3e-2 (fp8,
 where the oracle dequantises the same stored codes)."""
+import dataclasses
 import math
 
 import numpy as np
@@ -701,6 +702,26 @@ def test_grouped_heads(kv, q, D, bs, H, Hkv, ctx):
                               context_lens=ctx, kv_dtype=kv, q_dtype=q, spare_blocks=7,
                               salt=H * 7 + bs, max_blocks=int(W.blocks_needed(ctx, bs).max()) + 2)
     run_and_check(case, partitions=(0, -1, 64, 512))
+
+
+@pytest.mark.parametrize("H,Hkv,D", [(8, 1, 64), (16, 4, 128), (71, 1, 64), (40, 2, 128), (8, 8, 128)])
+def test_fp8_cache_bf16_queries_beyond_fp16_range(H, Hkv, D):
+    """bf16 queries whose entries reach ~1e5 .. 1e6 (fp16 stops at 65504) over an
+    fp8 cache: the codes are widened to the query's type, so the queries are used
+    as they are.  The queries are the seeded ones times 2^18 (exact in bf16) and
+    the softmax scale is divided by 2^18, so the weights stay those of ordinary
+    inputs and the comparison keeps the fp8 tolerance."""
+    ctx = [1, 37, 300, 1025]
+    case = W.make_decode_case(f"fp8_bigq_{H}x{Hkv}_{D}", "tiny", num_seqs=len(ctx), num_heads=H,
+                              num_kv_heads=Hkv, head_dim=D, block_size=16, context_lens=ctx,
+                              kv_dtype="fp8_e4m3", q_dtype="bf16", spare_blocks=5, salt=H + D)
+    f = torch.from_numpy(case.q.copy()).view(torch.bfloat16).float() * float(2 ** 18)
+    big = f.to(torch.bfloat16)
+    assert torch.equal(big.float(), f)                               # the scaling is exact
+    assert float(big.float().abs().max()) > 65504.0
+    case = dataclasses.replace(case, q=big.view(torch.int16).numpy().view(np.uint16),
+                               scale=case.scale / 2 ** 18)
+    run_and_check(case, partitions=(0, -1, 512))
 
 
 def test_grouped_heads_invalid_table_entries():
