@@ -507,7 +507,7 @@ class Llama7BPrefill(Workload):
 # launch configuration per workload: the fastest measured on MI355X (uniform
 # long contexts: one pass per (sequence, head); ragged batches: balanced split)
 DEFAULT_PARTITION = {"llama7b": 0, "opt13b": -1, "falcon7b": -1, "llama70b": -1, "tiny": 0,
-                     "llama7b_prefill": 0, "llama7b_int8": 0}
+                     "llama7b_prefill": 0, "llama7b_int8": 512}
 
 WORKLOADS = {"llama7b": Llama7B, "opt13b": Opt13B, "falcon7b": Falcon7B, "llama70b": Llama70B,
              "tiny": Tiny, "llama7b_prefill": Llama7BPrefill, "llama7b_int8": Llama7BInt8}
