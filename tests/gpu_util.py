@@ -103,3 +103,8 @@ def max_err(got: np.ndarray, ref: np.ndarray, out_dtype: str = None) -> float:
     if out_dtype is not None:
         err = np.maximum(err - half_ulp(ref, out_dtype), 0.0)
     return float(err.max(initial=0.0))
+
+
+def raw_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """Plain max-abs difference (no allowance for the output format's rounding)."""
+    return float(np.abs(got - ref).max(initial=0.0))

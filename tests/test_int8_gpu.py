@@ -77,13 +77,16 @@ def run_case(case, partitions):
     dev.write()
     torch.cuda.synchronize()
     check_pools(dev, kp, vp, ks, vs)
-    errs = {}
+    errs, raws = {}, {}
     for ps in partitions:
         out = dev.attend(ps)
         torch.cuda.synchronize()
-        errs[ps] = max_err(out_to_f64(out), ref, case.q_dtype)
+        got = out_to_f64(out)
+        errs[ps] = max_err(got, ref, case.q_dtype)
+        raws[ps] = float(np.abs(got - ref).max(initial=0.0))
         assert errs[ps] <= TOL_INT8, (case.name, ps, errs[ps])
     say(f"    max-abs error by partition size: {errs}")
+    say(f"    raw max-abs by partition size: {raws}")
 
 
 @pytest.mark.parametrize("q_dtype", ["f32", "f16", "bf16"])

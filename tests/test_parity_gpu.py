@@ -13,7 +13,7 @@ import oracle
 import paged_kv_cache_129_amd as pa
 import workloads as W
 from gpu_util import (TOL, DeviceCase, assert_pools_equal, from_dev, max_err, oracle_step,
-                      out_to_f64, say, to_dev)
+                      out_to_f64, raw_err, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,13 +34,16 @@ def run_and_check(case, partitions=(0,), label=""):
     dev.write()
     torch.cuda.synchronize()
     assert_pools_equal(dev, kp, vp)
-    errs = {}
+    errs, raws = {}, {}
     for ps in partitions:
         out = dev.attend(ps, out=torch.full_like(dev.q, float("nan")))   # every element written
         torch.cuda.synchronize()
-        errs[ps] = max_err(out_to_f64(out), ref, case.q_dtype)
+        got = out_to_f64(out)
+        errs[ps] = max_err(got, ref, case.q_dtype)
+        raws[ps] = raw_err(got, ref)
         assert errs[ps] <= TOL[case.kv_dtype], (case.name, ps, errs[ps])
     say(f"    max-abs error by partition size: {errs}")
+    say(f"    raw max-abs by partition size: {raws}")
     return dev, ref
 
 
@@ -107,8 +110,9 @@ def test_llama70b_gqa_shared_prompt_cow(full):
     for ps in (0, 512, -1):
         out = dev.attend(ps, out=torch.full_like(dev.q, float("nan")))
         torch.cuda.synchronize()
-        err = max_err(out_to_f64(out), ref, "bf16")
-        say(f"    partition {ps}: max-abs error {err:.3g}")
+        got = out_to_f64(out)
+        err = max_err(got, ref, "bf16")
+        say(f"    partition {ps}: max-abs error {err:.3g} (raw {raw_err(got, ref):.3g})")
         assert err <= TOL["bf16"]
 
 

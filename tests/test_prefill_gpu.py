@@ -75,7 +75,7 @@ def check(case, rows=None, label=""):
     assert np.isfinite(got).all(), "rows left unwritten or non-finite"
     sel = slice(None) if rows is None else np.asarray(rows)
     err = max_err(got[sel], ref[sel], case.q_dtype)
-    say(f"    max-abs error {err:.3g}")
+    say(f"    max-abs error {err:.3g} (raw {float(np.abs(got[sel] - ref[sel]).max(initial=0.0)):.3g})")
     assert err <= TOL[case.kv_dtype]
     return dev, got
 
