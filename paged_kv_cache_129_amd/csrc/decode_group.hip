@@ -55,10 +55,14 @@ void decode_group_kernel(DecodeArgs a) {
     constexpr int KPIECES = kGChunk * PPR;                       // pieces of a chunk's K rows
     constexpr int LPT = (2 * KPIECES + kGThreads - 1) / kGThreads;   // pieces per thread
     constexpr int HPP = 16 / EB;                                 // numbers per piece
-    // LDS row strides (halfs) of the widened tiles: K rows are read 16 bytes per
-    // lane by 16 rows at once (D + 8 spreads them over all banks), V rows by the
-    // transposing reads (D + 16 puts the rows of a pass 8 banks apart)
-    constexpr int LDK = D + 8;
+    // LDS row strides (halfs) of the widened tiles.  With rows D + 16 halfs apart
+    // (160 or 288 bytes) none of the tile's accesses waits on a bank conflict
+    // (measured with the LDS conflict counters): the 16-byte K reads of 16 rows at
+    // once, the transposing V reads of 16 rows, the 16-byte row-piece writes of a
+    // 16-bit cache, and the two 16-byte halves that a widened fp8 piece writes,
+    // provided that pieces whose index has bit 0 different from bit 2 write their
+    // upper half first.
+    constexpr int LDK = D + 16;
     constexpr int LDV = D + 16;
     constexpr int NC = D / 32;                                   // score MFMAs per half and chunk
     constexpr int NDT = D / 16;                                  // output d-tiles
@@ -181,13 +185,19 @@ void decode_group_kernel(DecodeArgs a) {
                             uint16_t* dst = isv ? &vt[buf][row * LDV + col * HPP]
                                                 : &kt[buf][row * LDK + col * HPP];
                             if constexpr (KVDT == PA_FP8_E4M3) {
+                                // half h0 (8 numbers from raw words 2 h0, 2 h0 + 1) first
+                                const int h0 = (col ^ (col >> 2)) & 1;
+                                const uint32_t r0 = st.ok[k] ? st.r[k].w[0] : 0u;
+                                const uint32_t r1 = st.ok[k] ? st.r[k].w[1] : 0u;
+                                const uint32_t r2 = st.ok[k] ? st.r[k].w[2] : 0u;
+                                const uint32_t r3 = st.ok[k] ? st.r[k].w[3] : 0u;
                                 uint32_t w[8];
-#pragma unroll
-                                for (int q = 0; q < 4; ++q) e4m3x4_widen<MT>(st.r[k].w[q], w[2 * q], w[2 * q + 1]);
-#pragma unroll
-                                for (int q = 0; q < 8; ++q) w[q] = st.ok[k] ? w[q] : 0u;
-                                *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
-                                *reinterpret_cast<uint4*>(dst + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+                                e4m3x4_widen<MT>(h0 ? r2 : r0, w[0], w[1]);
+                                e4m3x4_widen<MT>(h0 ? r3 : r1, w[2], w[3]);
+                                e4m3x4_widen<MT>(h0 ? r0 : r2, w[4], w[5]);
+                                e4m3x4_widen<MT>(h0 ? r1 : r3, w[6], w[7]);
+                                *reinterpret_cast<uint4*>(dst + 8 * h0) = make_uint4(w[0], w[1], w[2], w[3]);
+                                *reinterpret_cast<uint4*>(dst + 8 * (h0 ^ 1)) = make_uint4(w[4], w[5], w[6], w[7]);
                             } else {
                                 uint32_t w[4];
 #pragma unroll
