@@ -40,19 +40,19 @@ constexpr int kGTable = 1024;              // block-table entries staged per seg
 constexpr float kNegInfG = -__builtin_inff();
 constexpr float kSlack = 8.0f;             // log2 units a score may exceed the reference maximum by
 
-// KT tokens per step (a multiple of 32), NS steps' loads in flight, MINB
-// workgroups per CU that the register allocation must allow
+// KT tokens per step (64: four 16-token quarters), NS steps' loads in flight,
+// MINB workgroups per CU that the register allocation must allow
 template <int KVDT, int QDT, int D, int KT, int NS, int MINB>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(MINB * kGWaves / 4)))
 void decode_group_kernel(DecodeArgs a) {
-    constexpr int kGChunk = KT;
+    static_assert(KT == 64, "four 16-token quarters per step");
     // MFMA operand type: the cache's, or for an fp8 cache the query's (e4m3 widens
     // exactly to fp16 and to bf16, and a bf16 query keeps its range)
     constexpr int MT = (KVDT == PA_FP8_E4M3) ? QDT : KVDT;
     constexpr int EB = elem_bytes(KVDT);
     constexpr int RB = D * EB;                                   // bytes of a cached row
     constexpr int PPR = RB / 16;                                 // 16-byte pieces per row
-    constexpr int KPIECES = kGChunk * PPR;                       // pieces of a chunk's K rows
+    constexpr int KPIECES = KT * PPR;                            // pieces of a chunk's K rows
     constexpr int LPT = (2 * KPIECES + kGThreads - 1) / kGThreads;   // pieces per thread
     constexpr int HPP = 16 / EB;                                 // numbers per piece
     // LDS row strides (halfs) of the widened tiles.  With rows D + 16 halfs apart
@@ -64,13 +64,25 @@ void decode_group_kernel(DecodeArgs a) {
     // upper half first.
     constexpr int LDK = D + 16;
     constexpr int LDV = D + 16;
-    constexpr int NC = D / 32;                                   // score MFMAs per half and chunk
+    constexpr int NC = D / 32;                                   // score MFMAs per 16 tokens
     constexpr int NDT = D / 16;                                  // output d-tiles
+    constexpr int NQ = KT / 16;                                  // quarters per step
+    constexpr int TILE_HALFS = KT * LDK;
+    // merge of quarter results: per (split tile, quarter 1..3) the accumulators of
+    // a wavefront, then 16 maxima and 16 sums
+    constexpr int SLOT_FLOATS = NDT * 256 + 32;
+    constexpr int MERGE_SLOTS = (4 * TILE_HALFS * 2) / (SLOT_FLOATS * 4);
 
-    __shared__ __attribute__((aligned(16))) uint16_t kt[2][kGChunk * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t vt[2][kGChunk * LDV];
+    // both tile buffers of K, then both of V; after an item's last step, the
+    // merge slots
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[4 * TILE_HALFS];
     __shared__ int32_t tbl[kGTable];
+    // the number of the last table slice that holds an entry naming no block
+    // (slices are numbered per workgroup; no reset needed)
+    __shared__ int32_t tbl_bad;
     __shared__ __attribute__((aligned(8))) int32_t wl_lds[kListInts];
+    auto kt = [&](int buf) -> uint16_t* { return tiles + buf * TILE_HALFS; };
+    auto vt = [&](int buf) -> uint16_t* { return tiles + (2 + buf) * TILE_HALFS; };
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -78,12 +90,40 @@ void decode_group_kernel(DecodeArgs a) {
     const int j = lane >> 4;
     const int c16 = lane & 15;
     const int G = a.num_heads / a.num_kv_heads;
+    const int T = (G + 15) >> 4;                                 // 16-head tiles, 2..8
     const int bs = 1 << a.log2_bs;
     const char* kbase = reinterpret_cast<const char*>(a.k_pool);
     const char* vbase = reinterpret_cast<const char*>(a.v_pool);
-    const bool computes = 16 * wave < G;                         // wavefront-uniform
+
+    // Work of a step: T tiles x 4 quarters.  Wavefronts w and w + 4 share a SIMD,
+    // so the split keeps the four SIMDs even: a "full" wavefront takes one tile
+    // for every token; the four "split" wavefronts of a half of the workgroup
+    // take the same one or two tiles, each for one quarter of every step, and
+    // merge their results at the item's end (through LDS, in a fixed order).
+    //   T = 2: waves 0-3 tile 0, waves 4-7 tile 1, split   (per SIMD: 0.5 tile)
+    //   T = 5: waves 0-3 full tiles 0-3, waves 4-7 tile 4, split (1.25)
+    //   otherwise wave w full tile w (T = 3, 4: 1; T = 6, 7, 8: 2 on the busiest SIMD)
+    constexpr int kSMax = 1;                                     // tiles of a wavefront
+    const int n_split_tiles = T == 2 ? 2 : (T == 5 ? 1 : 0);
+    const bool wg_splits = n_split_tiles > 0 && 3 * n_split_tiles <= MERGE_SLOTS;
+    const int split_base = T >= 4 ? 4 : 0;
+    bool full;
+    int tile0, ntiles, quarter = 0;
+    if (!wg_splits || (wave < 4 && T >= 4)) {
+        full = true;
+        tile0 = wave;
+        ntiles = wave < T ? 1 : 0;
+    } else {
+        full = false;
+        quarter = wave & 3;
+        tile0 = T == 2 ? wave >> 2 : 4;
+        ntiles = 1;
+    }
+    const bool computes = ntiles > 0;                            // wavefront-uniform
 
     Schedule<kGThreads> sch;
+    int slice_no = 0;                                            // table slices staged so far
+    if (tid == 0) tbl_bad = -1;
     for (int s0 = 0; s0 < a.num_seqs; s0 += kWindow) {
         sch.build(a, s0, min(kWindow, a.num_seqs - s0), a.units, wl_lds, (int)blockIdx.x,
                   (int)gridDim.x, tid == 0);
@@ -104,35 +144,42 @@ void decode_group_kernel(DecodeArgs a) {
             const int kvh = cur.unit;                            // one unit per KV head
             const int t0 = cur.t0, t1 = cur.t1;
             const int32_t* trow = a.tables + (int64_t)s * a.max_blocks;
-            const int hu = 16 * wave + c16;                      // this lane's head column
-            const bool hlive = hu < G;
 
-            // B operands of the score MFMA: Q^T[d][head], head dimensions 32 c + 8 j..
-            Op8 qop[NC];
-            {
+            // B operands of the score MFMA per tile: Q^T[d][head], head dimensions
+            // 32 c + 8 j..; state per tile: reference maximum, running sum, O^T
+            Op8 qop[kSMax][NC];
+            float m[kSMax], l[kSMax];
+            f32x4 acc[kSMax][NDT];
+#pragma unroll
+            for (int ti = 0; ti < kSMax; ++ti) {
+                const int hu = 16 * (tile0 + ti) + c16;
+                const bool hlive = ti < ntiles && hu < G;
                 const char* qrow = reinterpret_cast<const char*>(a.q) +
                                    ((int64_t)s * a.num_heads + kvh * G + (hlive ? hu : 0)) * D *
                                        elem_bytes(QDT);
 #pragma unroll
                 for (int c = 0; c < NC; ++c) {
                     static_assert(QDT == MT, "the query is an MFMA operand as it is");
-                    const Raw16 r = load16(qrow + (32 * c + 8 * j) * elem_bytes(QDT));
-                    Op8 o;
+                    Op8 o{{0u, 0u, 0u, 0u}};
+                    if (ti < ntiles) {                           // wavefront-uniform
+                        const Raw16 r = load16(qrow + (32 * c + 8 * j) * elem_bytes(QDT));
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) o.w[q] = hlive ? r.w[q] : 0u;
-                    qop[c] = o;
+                        for (int q = 0; q < 4; ++q) o.w[q] = hlive ? r.w[q] : 0u;
+                    }
+                    qop[ti][c] = o;
                 }
-            }
-
-            float m = kNegInfG, l = 0.0f;
-            f32x4 acc[NDT];
+                m[ti] = kNegInfG;
+                l[ti] = 0.0f;
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int dt = 0; dt < NDT; ++dt) acc[ti][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
 
             const int b_first = t0 >> a.log2_bs;
             const int b_end = (t1 + bs - 1) >> a.log2_bs;
             __syncthreads();                                     // the previous item's table is read
-            tpre.store(tbl, min(b_end, b_first + kGTable) - b_first, a.num_blocks, tid);
+            ++slice_no;
+            if (tpre.store(tbl, min(b_end, b_first + kGTable) - b_first, a.num_blocks, tid))
+                tbl_bad = slice_no;
             __syncthreads();
             have = sch.next(a, itm);
             if (have) prefetch(itm);
@@ -140,15 +187,28 @@ void decode_group_kernel(DecodeArgs a) {
                 const int se = min(b_end, sb + kGTable);
                 if (sb != b_first) {                             // later slices of a long item
                     __syncthreads();
+                    ++slice_no;
                     for (int i = tid; i < se - sb; i += kGThreads) {
                         const int b = trow[sb + i];
-                        tbl[i] = (b >= 0 && b < a.num_blocks) ? b : -1;
+                        const bool ok = b >= 0 && b < a.num_blocks;
+                        tbl[i] = ok ? b : -1;
+                        if (!ok) tbl_bad = slice_no;
                     }
                     __syncthreads();
                 }
+                // every block of the slice is valid: steps that end inside the
+                // item's tokens have all their tokens present
+                const bool slice_ok = uni(tbl_bad) != slice_no;
                 const int ts = max(t0, sb << a.log2_bs);
                 const int te = min(t1, se << a.log2_bs);
-                const int nch = (te - ts + kGChunk - 1) / kGChunk;
+                const int nch = (te - ts + KT - 1) / KT;
+                // tokens c0 .. c0 + KT - 1 of the slice that are present (in the item
+                // and in a valid block), as a mask (one look at the table per lane)
+                auto chunk_mask = [&](int c0) -> uint64_t {
+                    const int t = c0 + lane;
+                    const bool ok = lane < KT && t < te && tbl[(min(t, te - 1) >> a.log2_bs) - sb] >= 0;
+                    return __builtin_amdgcn_ballot_w64(ok);
+                };
 
                 // this thread's pieces of chunk n: raw bytes in one register stage
                 struct Stage {
@@ -156,7 +216,7 @@ void decode_group_kernel(DecodeArgs a) {
                     bool ok[LPT];
                 };
                 auto load_chunk = [&](Stage& st, int n) {
-                    const int c0 = ts + n * kGChunk;
+                    const int c0 = ts + n * KT;
 #pragma unroll
                     for (int k = 0; k < LPT; ++k) {
                         const int p = tid + k * kGThreads;
@@ -182,8 +242,8 @@ void decode_group_kernel(DecodeArgs a) {
                             const bool isv = p >= KPIECES;
                             const int pl = isv ? p - KPIECES : p;
                             const int row = pl / PPR, col = pl % PPR;
-                            uint16_t* dst = isv ? &vt[buf][row * LDV + col * HPP]
-                                                : &kt[buf][row * LDK + col * HPP];
+                            uint16_t* dst = isv ? vt(buf) + row * LDV + col * HPP
+                                                : kt(buf) + row * LDK + col * HPP;
                             if constexpr (KVDT == PA_FP8_E4M3) {
                                 // half h0 (8 numbers from raw words 2 h0, 2 h0 + 1) first
                                 const int h0 = (col ^ (col >> 2)) & 1;
@@ -207,104 +267,149 @@ void decode_group_kernel(DecodeArgs a) {
                         }
                     }
                 };
-                // 32 tokens (rows r0.. of tile buffer `buf`) of this wavefront's tile
-                auto compute32 = [&](int c0, int buf, int r0) {
-                    // present tokens of the chunk as a 32-bit mask (the same in every lane)
-                    uint32_t present;
-                    {
-                        const int t = c0 + (lane & 31);
-                        const bool ok = t < te && tbl[(min(t, te - 1) >> a.log2_bs) - sb] >= 0;
-                        present = (uint32_t)__builtin_amdgcn_ballot_w64(ok && lane < 32);
+                // Online-softmax update of tile ti with the scores sc[0..nv) of chunk
+                // c0 (value e is token c0 + bit(e)) into weights pr: one maximum, one
+                // check of the reference maximum (the accumulators are rescaled only
+                // when a score passes it by more than kSlack).  Unless every token is
+                // present (`fast`), absent ones are masked; the mask is built inside
+                // the masked branches only, so that none of its work reaches the
+                // common path.
+                auto softmax = [&](int ti, const f32x4* sc, float* pr, int nv, bool fast, int c0,
+                                   auto&& bit) {
+                    float lm = kNegInfG;
+                    if (fast) {
+                        for (int e = 0; e < nv; ++e) lm = fmaxf(lm, sc[e >> 2][e & 3]);
+                        lm *= a.qk_scale;
+                    } else {
+                        const uint64_t pm = chunk_mask(c0);
+                        for (int e = 0; e < nv; ++e)
+                            lm = fmaxf(lm, ((pm >> bit(e)) & 1ull) ? sc[e >> 2][e & 3] * a.qk_scale : kNegInfG);
                     }
-                    f32x4 sc[2];
+                    if (__builtin_amdgcn_ballot_w64(lm > m[ti] + kSlack)) {   // rare after the first step
+                        const float mx = max_over_groups(lm);
+                        const float mn = (mx > m[ti] + kSlack) ? mx : m[ti];
+                        const float alpha = mn != m[ti] ? fast_exp2(m[ti] - mn) : 1.0f;   // from -inf: 0
+                        if (__builtin_amdgcn_ballot_w64(mn != m[ti])) {
 #pragma unroll
-                    for (int u = 0; u < 2; ++u) {
+                            for (int dt = 0; dt < NDT; ++dt) acc[ti][dt] *= alpha;
+                            l[ti] *= alpha;
+                        }
+                        m[ti] = mn;
+                    }
+                    for (int e = 0; e < nv; ++e) pr[e] = fast_exp2(fmaf(sc[e >> 2][e & 3], a.qk_scale, -m[ti]));
+                    if (!fast) {                                 // absent tokens weigh nothing
+                        const uint64_t pm = chunk_mask(c0);
+                        for (int e = 0; e < nv; ++e) pr[e] = ((pm >> bit(e)) & 1ull) ? pr[e] : 0.0f;
+                    }
+                };
+                // the running sum adds four weights as the matrix cores see them; the
+                // bf16 low parts (weights minus their bf16 roundings) go to `lo`
+                auto pack4 = [&](int ti, const float* pg, uint32_t* hi, uint32_t* lo) {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) hi[q] = pack2<MT>(pg[2 * q], pg[2 * q + 1]);
+                    if constexpr (MT == PA_F16) {
+#pragma unroll
+                        for (int q = 0; q < 2; ++q)
+                            l[ti] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, hi[q]),
+                                                           half2_t{(_Float16)1.0f, (_Float16)1.0f}, l[ti], false);
+                    } else {
+                        l[ti] += (pg[0] + pg[1]) + (pg[2] + pg[3]);
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const float h0 = __uint_as_float(hi[q] << 16);
+                            const float h1 = __uint_as_float(hi[q] & 0xFFFF0000u);
+                            lo[q] = pack2<MT>(pg[2 * q] - h0, pg[2 * q + 1] - h1);
+                        }
+                    }
+                };
+
+                // A full wavefront's step: the KT tokens of chunk n for tile 0, every
+                // score first (the K reads and MFMAs of all quarters back to back),
+                // one softmax update, then O^T[d][head] += V^T P^T with 32 tokens per
+                // MFMA (quarters 2g, 2g + 1 side by side form the B operand P^T).
+                auto full_step = [&](int c0, int buf, bool fast) {
+                    f32x4 sc[NQ];
+#pragma unroll
+                    for (int u = 0; u < NQ; ++u) {
                         sc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int c = 0; c < NC; ++c) {
                             const uint4 r = *reinterpret_cast<const uint4*>(
-                                &kt[buf][(r0 + 16 * u + c16) * LDK + 32 * c + 8 * j]);
+                                kt(buf) + (16 * u + c16) * LDK + 32 * c + 8 * j);
                             const Op8 kop{{r.x, r.y, r.z, r.w}};
-                            sc[u] = mma32<MT>(kop, qop[c], sc[u]);
+                            sc[u] = mma32<MT>(kop, qop[0][c], sc[u]);
                         }
                     }
-                    // value e = 4u + i is token c0 + 16u + 4j + i
-                    const bool fast = present == 0xFFFFFFFFu && a.qk_scale > 0.0f;
-                    float pr[8];
-                    float lm = kNegInfG;
-                    if (fast) {
+                    float pr[4 * NQ];
+                    softmax(0, sc, pr, 4 * NQ, fast, c0,
+                            [&](int e) { return 16 * (e >> 2) + 4 * j + (e & 3); });
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) lm = fmaxf(lm, sc[e >> 2][e & 3]);
-                        lm *= a.qk_scale;
-                    } else {
+                    for (int g = 0; g < NQ / 2; ++g) {
+                        Op8 pop, plo;
+                        pack4(0, pr + 8 * g, pop.w, plo.w);
+                        pack4(0, pr + 8 * g + 4, pop.w + 2, plo.w + 2);
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const bool lv = (present >> (16 * (e >> 2) + 4 * j + (e & 3))) & 1u;
-                            lm = fmaxf(lm, lv ? sc[e >> 2][e & 3] * a.qk_scale : kNegInfG);
+                        for (int dt = 0; dt < NDT; ++dt) {
+                            const uint16_t* vp =
+                                vt(buf) + (32 * g + 4 * j + (c16 >> 2)) * LDV + 16 * dt + 4 * (c16 & 3);
+                            const Op4 v0 = read_tr16(vp);
+                            const Op4 v1 = read_tr16(vp + 16 * LDV);
+                            const Op8 vop{{v0.w[0], v0.w[1], v1.w[0], v1.w[1]}};
+                            acc[0][dt] = mma32<MT>(vop, pop, acc[0][dt]);
+                            if constexpr (MT == PA_BF16) acc[0][dt] = mma32<MT>(vop, plo, acc[0][dt]);
                         }
                     }
-                    if (__builtin_amdgcn_ballot_w64(lm > m + kSlack)) {   // rare after the first chunk
-                        const float mx = max_over_groups(lm);
-                        const float mn = (mx > m + kSlack) ? mx : m;
-                        const float alpha = mn != m ? fast_exp2(m - mn) : 1.0f;   // from -inf: 0
-                        if (__builtin_amdgcn_ballot_w64(mn != m)) {
+                };
+                // A split wavefront's step: quarter `quarter` of chunk n (16 tokens)
+                // for each of its tiles; P V on the 16-token MFMA.
+                auto split_step = [&](int c0, int buf, bool fast) {
+                    const int r0 = 16 * quarter;
+                    Op8 kop[NC];
 #pragma unroll
-                            for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-                            l *= alpha;
-                        }
-                        m = mn;
+                    for (int c = 0; c < NC; ++c) {
+                        const uint4 r = *reinterpret_cast<const uint4*>(
+                            kt(buf) + (r0 + c16) * LDK + 32 * c + 8 * j);
+                        kop[c] = Op8{{r.x, r.y, r.z, r.w}};
                     }
-                    if (fast) {
+                    Op4 vop[NDT];
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(fmaf(sc[e >> 2][e & 3], a.qk_scale, -m));
-                    } else {
+                    for (int dt = 0; dt < NDT; ++dt)
+                        vop[dt] = read_tr16(vt(buf) + (r0 + 4 * j + (c16 >> 2)) * LDV + 16 * dt + 4 * (c16 & 3));
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const bool lv = (present >> (16 * (e >> 2) + 4 * j + (e & 3))) & 1u;
-                            pr[e] = lv ? fast_exp2(fmaf(sc[e >> 2][e & 3], a.qk_scale, -m)) : 0.0f;
+                    for (int ti = 0; ti < kSMax; ++ti) {
+                        if (ti < ntiles) {                       // wavefront-uniform
+                            f32x4 sc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                            for (int c = 0; c < NC; ++c) sc[0] = mma32<MT>(kop[c], qop[ti][c], sc[0]);
+                            float pr[4];
+                            softmax(ti, sc, pr, 4, fast, c0, [&](int e) { return r0 + 4 * j + e; });
+                            Op4 pop, plo;
+                            pack4(ti, pr, pop.w, plo.w);
+#pragma unroll
+                            for (int dt = 0; dt < NDT; ++dt) {
+                                acc[ti][dt] = mma16<MT>(vop[dt], pop, acc[ti][dt]);
+                                if constexpr (MT == PA_BF16) acc[ti][dt] = mma16<MT>(vop[dt], plo, acc[ti][dt]);
+                            }
                         }
-                    }
-                    // weights -> the B operand P^T (tokens 4j.. of each half); the running
-                    // sum adds them as the matrix cores see them
-                    Op8 pop, plo;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) pop.w[q] = pack2<MT>(pr[2 * q], pr[2 * q + 1]);
-                    if constexpr (MT == PA_F16) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            l = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pop.w[q]),
-                                                       half2_t{(_Float16)1.0f, (_Float16)1.0f}, l, false);
-                    } else {
-                        l += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float h0 = __uint_as_float(pop.w[q] << 16);
-                            const float h1 = __uint_as_float(pop.w[q] & 0xFFFF0000u);
-                            plo.w[q] = pack2<MT>(pr[2 * q] - h0, pr[2 * q + 1] - h1);
-                        }
-                    }
-                    // O^T[d][head] += V^T[d][token] P^T[token][head], 32 tokens per MFMA
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        const uint16_t* vp = &vt[buf][(r0 + 4 * j + (c16 >> 2)) * LDV + 16 * dt + 4 * (c16 & 3)];
-                        const Op4 v0 = read_tr16(vp);
-                        const Op4 v1 = read_tr16(vp + 16 * LDV);
-                        const Op8 vop{{v0.w[0], v0.w[1], v1.w[0], v1.w[1]}};
-                        acc[dt] = mma32<MT>(vop, pop, acc[dt]);
-                        if constexpr (MT == PA_BF16) acc[dt] = mma32<MT>(vop, plo, acc[dt]);
                     }
                 };
                 auto compute_chunk = [&](int n, int buf) {
-#pragma unroll
-                    for (int g = 0; g < KT / 32; ++g) compute32(ts + n * KT + 32 * g, buf, 32 * g);
+                    const int c0 = ts + n * KT;
+                    // all KT tokens present (known without a look at the table when
+                    // the slice is clean and the step ends inside the item)
+                    const bool fast = slice_ok && c0 + KT <= te && a.qk_scale > 0.0f;
+                    if (full) full_step(c0, buf, fast);
+                    else split_step(c0, buf, fast);
                 };
 
                 // Pipeline: register stage n mod NS holds chunk n from its load until it
                 // is written to tile buffer n mod 2; step n writes chunk n + 1, loads
                 // chunk n + NS into the stage just freed (past the end: masked loads of
-                // the pool's first bytes, so that no branch sits between a load and its
-                // wait), computes chunk n and ends with the barrier that hands both
-                // buffers over.
+                // the pool's first bytes), computes chunk n and ends with the barrier
+                // that hands both buffers over.  Every step of the unrolled group
+                // issues its loads, also the steps past the last chunk: with a branch
+                // around a load, the compiler could no longer count the loads issued
+                // after the one a write waits for, and would wait for all of them.
                 Stage ring[NS];
 #pragma unroll
                 for (int k = 0; k < NS; ++k) load_chunk(ring[k], k);
@@ -314,9 +419,10 @@ void decode_group_kernel(DecodeArgs a) {
 #pragma unroll
                     for (int k = 0; k < NS; ++k) {
                         const int n = n0 + k;
-                        if (n < nch) {
-                            write_chunk(ring[(k + 1) % NS], (n + 1) & 1);
-                            load_chunk(ring[k], n + NS);
+                        const bool live = n < nch;               // workgroup-uniform
+                        if (live) write_chunk(ring[(k + 1) % NS], (n + 1) & 1);
+                        load_chunk(ring[k], n + NS);
+                        if (live) {
                             if (computes) compute_chunk(n, n & 1);
                             __syncthreads();
                         }
@@ -324,31 +430,94 @@ void decode_group_kernel(DecodeArgs a) {
                 }
             }
 
-            // ---- per-column totals, then this tile's result for its item
-            if (computes) {
-                const float lt = sum_over_groups(l);
-                if (hlive) {
-                    const int head = kvh * G + hu;
-                    const float inv_l = lt > 0.0f ? 1.0f / lt : 0.0f;
-                    const int64_t r = cur.rec0 + (int64_t)hu * cur.rec_stride;
-                    if (!cur.whole && j == 0) {
-                        a.ws[r] = m;
-                        a.ws[a.nrec + r] = lt;
+            // ---- per-column totals; the split wavefronts of a tile merge their
+            // quarters into quarter 0's: maxima, then the sums and accumulators,
+            // each scaled to the common maximum, added in quarter order
+            float lt[kSMax];
+#pragma unroll
+            for (int ti = 0; ti < kSMax; ++ti) lt[ti] = sum_over_groups(l[ti]);
+            if (wg_splits) {
+                float* slots = reinterpret_cast<float*>(tiles);
+                auto slot = [&](int ti, int q) -> float* {
+                    return slots + ((tile0 + ti - split_base) * 3 + (q - 1)) * SLOT_FLOATS;
+                };
+                if (!full && quarter != 0) {
+#pragma unroll
+                    for (int ti = 0; ti < kSMax; ++ti) {
+                        if (ti < ntiles) {
+                            float* sp = slot(ti, quarter);
+#pragma unroll
+                            for (int dt = 0; dt < NDT; ++dt)
+                                *reinterpret_cast<f32x4*>(sp + (dt * 64 + lane) * 4) = acc[ti][dt];
+                            if (j == 0) {
+                                sp[NDT * 256 + c16] = m[ti];
+                                sp[NDT * 256 + 16 + c16] = lt[ti];
+                            }
+                        }
                     }
+                }
+                __syncthreads();
+                if (!full && quarter == 0) {
 #pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        const int d = 16 * dt + 4 * j;
-                        if (cur.whole) {
-                            const float f = inv_l * a.out_scale;
-                            char* op = reinterpret_cast<char*>(a.out) +
-                                       (((int64_t)s * a.num_heads + head) * D + d) * elem_bytes(QDT);
-                            *reinterpret_cast<uint2*>(op) =
-                                make_uint2(pack2<QDT>(acc[dt][0] * f, acc[dt][1] * f),
-                                           pack2<QDT>(acc[dt][2] * f, acc[dt][3] * f));
-                        } else {
-                            float* wo = a.ws + 2 * a.nrec + r * D + d;
+                    for (int ti = 0; ti < kSMax; ++ti) {
+                        if (ti < ntiles) {
+                            float mq[4], f[4];
+                            mq[0] = m[ti];
+                            float mm = m[ti];
 #pragma unroll
-                            for (int i = 0; i < 4; ++i) wo[i] = acc[dt][i] * inv_l;
+                            for (int q = 1; q < 4; ++q) {
+                                mq[q] = slot(ti, q)[NDT * 256 + c16];
+                                mm = fmaxf(mm, mq[q]);
+                            }
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) f[q] = mq[q] == kNegInfG ? 0.0f : fast_exp2(mq[q] - mm);
+                            float tot = lt[ti] * f[0];
+#pragma unroll
+                            for (int q = 1; q < 4; ++q) tot += slot(ti, q)[NDT * 256 + 16 + c16] * f[q];
+#pragma unroll
+                            for (int dt = 0; dt < NDT; ++dt) {
+                                f32x4 o = acc[ti][dt] * f[0];
+#pragma unroll
+                                for (int q = 1; q < 4; ++q)
+                                    o += *reinterpret_cast<const f32x4*>(slot(ti, q) + (dt * 64 + lane) * 4) * f[q];
+                                acc[ti][dt] = o;
+                            }
+                            m[ti] = mm;
+                            lt[ti] = tot;
+                        }
+                    }
+                }
+            }
+
+            // ---- this wavefront's results for its item: quarter 0 of a split tile,
+            // or a full tile
+            if (computes && (full || quarter == 0)) {
+#pragma unroll
+                for (int ti = 0; ti < kSMax; ++ti) {
+                    const int hu = 16 * (tile0 + ti) + c16;
+                    if (ti < ntiles && hu < G) {
+                        const int head = kvh * G + hu;
+                        const float inv_l = lt[ti] > 0.0f ? 1.0f / lt[ti] : 0.0f;
+                        const int64_t r = cur.rec0 + (int64_t)hu * cur.rec_stride;
+                        if (!cur.whole && j == 0) {
+                            a.ws[r] = m[ti];
+                            a.ws[a.nrec + r] = lt[ti];
+                        }
+#pragma unroll
+                        for (int dt = 0; dt < NDT; ++dt) {
+                            const int d = 16 * dt + 4 * j;
+                            if (cur.whole) {
+                                const float f = inv_l * a.out_scale;
+                                char* op = reinterpret_cast<char*>(a.out) +
+                                           (((int64_t)s * a.num_heads + head) * D + d) * elem_bytes(QDT);
+                                *reinterpret_cast<uint2*>(op) =
+                                    make_uint2(pack2<QDT>(acc[ti][dt][0] * f, acc[ti][dt][1] * f),
+                                               pack2<QDT>(acc[ti][dt][2] * f, acc[ti][dt][3] * f));
+                            } else {
+                                float* wo = a.ws + 2 * a.nrec + r * D + d;
+#pragma unroll
+                                for (int i = 0; i < 4; ++i) wo[i] = acc[ti][dt][i] * inv_l;
+                            }
                         }
                     }
                 }
@@ -357,15 +526,14 @@ void decode_group_kernel(DecodeArgs a) {
     }
 }
 
-// Measured on Falcon-7B's layer (71 heads of 64, fp8): 64-token steps with
-// four in flight and two workgroups per CU beat 32-token steps (three to six
-// in flight) and one workgroup per CU by 3-12%.
+// Measured on Falcon-7B's layer (71 heads of 64, fp8): 64-token steps with four
+// in flight; registers for one workgroup per CU (no spills) beat two workgroups
+// per CU with the registers capped at 128 (spilling) by 5%.
 template <int KVDT, int QDT, int D>
 hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
     constexpr int KT = 64;                              // tokens per step
     constexpr int NS = 4;                               // steps in flight per workgroup
-    // workgroups per CU the registers must allow (fp8, 64 dimensions: two fit)
-    constexpr int MINB = (D == 64 && KVDT == PA_FP8_E4M3) ? 2 : 1;
+    constexpr int MINB = 1;                             // workgroups per CU the registers must allow
     auto kernel = decode_group_kernel<KVDT, QDT, D, KT, NS, MINB>;
     a.unit_heads = a.num_heads / a.num_kv_heads;        // a unit: every query head of a KV head
     a.units_per_kv = 1;

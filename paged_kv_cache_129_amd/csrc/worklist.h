@@ -398,12 +398,19 @@ struct TablePrefetch {
             v[k] = trow[min(b_first + min(i, span - 1), max_blocks - 1)];
         }
     }
-    __device__ __forceinline__ void store(int32_t* tbl, int n, int num_blocks, int t) const {
+    // returns whether this thread stored an entry that names no block
+    __device__ __forceinline__ bool store(int32_t* tbl, int n, int num_blocks, int t) const {
+        bool bad = false;
 #pragma unroll
         for (int k = 0; k < TP; ++k) {
             const int i = k * NT + t;
-            if (i < n) tbl[i] = (v[k] >= 0 && v[k] < num_blocks) ? v[k] : -1;
+            if (i < n) {
+                const bool ok = v[k] >= 0 && v[k] < num_blocks;
+                tbl[i] = ok ? v[k] : -1;
+                bad |= !ok;
+            }
         }
+        return bad;
     }
 };
 
