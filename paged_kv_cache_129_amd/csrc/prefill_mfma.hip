@@ -55,8 +55,13 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
     static_assert(NLI * NW * RPI == kKT, "chunk split");
 
     // K and V chunks, double-buffered, rows of ROWB bytes with no padding: piece p
-    // of row r is stored at piece slot p ^ (r % PPR), so that the 16 rows of a
-    // K-operand read and the 4 rows of a transposed V read hit distinct banks.
+    // of row r is stored at piece slot p ^ swz(r).  The 16 rows of a K-operand read
+    // then take 16 distinct slots.  A transposed V read takes 8 bytes from two
+    // adjacent pieces of four rows 4 j.. 4 j + 3 per 16 lanes: with 256-byte rows
+    // (128 dimensions) the slots must also differ above bit 0 across those rows,
+    // which the row index rotated left by one bit gives (r % 16 has the two rows'
+    // adjacent pieces collide in pairs, 2-way bank conflicts); with 128-byte rows
+    // the row parity already separates them.
     // Chunks arrive by direct global-to-LDS loads (no registers in between).
     __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][kKT * ROWB];
     __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][kKT * ROWB];
@@ -69,6 +74,10 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
     const int c16 = lane & 15;
     const int G = a.num_heads / a.num_kv_heads;
     const int bs = 1 << a.log2_bs;
+    auto swz = [](int r) -> int {
+        if constexpr (PPR == 16) return ((r << 1) & 14) | ((r >> 3) & 1);
+        return r % PPR;
+    };
 
     // item: KV head fastest, then sequence, then column block (last blocks first)
     int bid = blockIdx.x;
@@ -125,7 +134,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
     // ---- chunk loader.  Load instruction k of wavefront w fills rows
     // (w * NLI + k) * RPI .. + RPI - 1 of a chunk: lane i lands in piece slot i % PPR
     // of row i / PPR (a direct load writes lane i's 16 bytes at base + 16 i), so it
-    // fetches the piece that belongs there, (i % PPR) ^ (row % PPR).
+    // fetches the piece that belongs there, (i % PPR) ^ swz(row).
     const char* kbase = reinterpret_cast<const char*>(a.k_pool);
     const char* vbase = reinterpret_cast<const char*>(a.v_pool);
     const int wu = __builtin_amdgcn_readfirstlane(wave);
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
 #pragma unroll
     for (int k = 0; k < NLI; ++k) {
         lrow[k] = (wu * NLI + k) * RPI + lane / PPR;
-        lpiece[k] = (uint32_t)(lslot ^ (lrow[k] % PPR)) * 16u;
+        lpiece[k] = (uint32_t)(lslot ^ swz(lrow[k])) * 16u;
     }
     int blk_next[NLI];                   // block ids of the rows of the next chunk to load
     // table loads are branch-free (index clamped into range) so that the compiler's
@@ -233,7 +242,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
 #pragma unroll
                 for (int cc = 0; cc < NC; ++cc) {
                     const uint4 r = *reinterpret_cast<const uint4*>(
-                        &kt[row * ROWB + (((4 * cc + j) ^ (row % PPR)) * 16)]);
+                        &kt[row * ROWB + (((4 * cc + j) ^ swz(row)) * 16)]);
                     const Op8 kop{{r.x, r.y, r.z, r.w}};
 #pragma unroll
                     for (int tt = 0; tt < TQ; ++tt) sc[tt][h] = mma32<DT>(kop, qop[tt][cc], sc[tt][h]);
@@ -341,9 +350,9 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
                     const int rr = 32 * sub + 4 * j + (c16 >> 2);
                     const int pc = 2 * dt + ((c16 & 3) >> 1), hb = (c16 & 1) * 8;
                     const Op4 v0 = read_tr16(reinterpret_cast<const uint16_t*>(
-                        &vt[rr * ROWB + ((pc ^ (rr % PPR)) * 16) + hb]));
+                        &vt[rr * ROWB + ((pc ^ swz(rr)) * 16) + hb]));
                     const Op4 v1 = read_tr16(reinterpret_cast<const uint16_t*>(
-                        &vt[(rr + 16) * ROWB + ((pc ^ ((rr + 16) % PPR)) * 16) + hb]));
+                        &vt[(rr + 16) * ROWB + ((pc ^ swz(rr + 16)) * 16) + hb]));
                     vop.w[0] = v0.w[0];
                     vop.w[1] = v0.w[1];
                     vop.w[2] = v1.w[0];
