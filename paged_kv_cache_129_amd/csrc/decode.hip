@@ -547,7 +547,10 @@ hipError_t launch_decode(DecodeArgs& a, int q_dt, int kv_dt, int head_dim,
                          hipStream_t stream) {
     const int group = a.num_heads / a.num_kv_heads;
     hipError_t e;
-    if (decode_group_supported(q_dt, kv_dt, head_dim, group))
+    // the large-group kernel addresses a pool block (every KV head's rows) in 32 bits
+    const uint64_t block_bytes = ((uint64_t)a.num_kv_heads << a.log2_bs) * (uint64_t)head_dim *
+                                 (uint64_t)elem_bytes(kv_dt);
+    if (decode_group_supported(q_dt, kv_dt, head_dim, group) && block_bytes < ((uint64_t)1 << 32))
         e = launch_decode_group(a, q_dt, kv_dt, head_dim, stream);
     else if (decode_mfma_supported(q_dt, kv_dt, head_dim, group))
         e = launch_decode_mfma(a, q_dt, kv_dt, head_dim, stream);

@@ -94,6 +94,7 @@ void decode_group_kernel(DecodeArgs a) {
     const int bs = 1 << a.log2_bs;
     const char* kbase = reinterpret_cast<const char*>(a.k_pool);
     const char* vbase = reinterpret_cast<const char*>(a.v_pool);
+    const uint32_t blk_bytes = ((uint32_t)a.num_kv_heads << a.log2_bs) * (uint32_t)RB;
 
     // Work of a step: T tiles x 4 quarters.  Wavefronts w and w + 4 share a SIMD,
     // so the split keeps the four SIMDs even: a "full" wavefront takes one tile
@@ -216,23 +217,26 @@ void decode_group_kernel(DecodeArgs a) {
                     bool ok[LPT];
                 };
                 auto load_chunk = [&](Stage& st, int n) {
-                    const int c0 = ts + n * KT;
-#pragma unroll
-                    for (int k = 0; k < LPT; ++k) {
-                        const int p = tid + k * kGThreads;
-                        const bool isv = p >= KPIECES;
-                        const int pl = isv ? p - KPIECES : p;
-                        const int row = pl / PPR, col = pl % PPR;
-                        const int t = c0 + row;
-                        const bool in = p < 2 * KPIECES && t < te;
-                        const int blk = in ? tbl[(t >> a.log2_bs) - sb] : -1;
-                        st.ok[k] = blk >= 0;
-                        const int64_t r = ((((int64_t)(blk >= 0 ? blk : 0)) * a.num_kv_heads + kvh)
-                                           << a.log2_bs) + (t & (bs - 1));
-                        const char* src = (isv ? vbase : kbase) + (blk >= 0 ? r * RB + col * 16 : 0);
-                        st.r[k] = load16_stream(src);
-                    }
-                };
+            const int c0 = ts + n * KT;
+        #pragma unroll
+            for (int k = 0; k < LPT; ++k) {
+                const int p = tid + k * kGThreads;
+                const bool isv = p >= KPIECES;
+                const int pl = isv ? p - KPIECES : p;
+                const int row = pl / PPR, col = pl % PPR;
+                const int t = c0 + row;
+                const bool in = p < 2 * KPIECES && t < te;
+                const int blk = in ? tbl[(t >> a.log2_bs) - sb] : -1;
+                st.ok[k] = blk >= 0;
+                // byte offset: block * (bytes of a block) + this KV head's rows + the
+                // token's row + the piece (the launch keeps a block's bytes below
+                // 2^32: one 32 x 32 -> 64-bit multiply-add)
+                const uint32_t within =
+                    ((((uint32_t)kvh << a.log2_bs) + (uint32_t)(t & (bs - 1))) * (uint32_t)RB) + (uint32_t)col * 16u;
+                const uint64_t off = blk >= 0 ? (uint64_t)(uint32_t)blk * blk_bytes + within : 0u;
+                st.r[k] = load16_stream((isv ? vbase : kbase) + off);
+            }
+        };
                 // widen a stage into tile buffer `buf` (absent rows as zeros)
                 auto write_chunk = [&](const Stage& st, int buf) {
 #pragma unroll
