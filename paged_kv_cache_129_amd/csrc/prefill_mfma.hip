@@ -55,13 +55,14 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
     static_assert(NLI * NW * RPI == kKT, "chunk split");
 
     // K and V chunks, double-buffered, rows of ROWB bytes with no padding: piece p
-    // of row r is stored at piece slot p ^ swz(r).  The 16 rows of a K-operand read
-    // then take 16 distinct slots.  A transposed V read takes 8 bytes from two
-    // adjacent pieces of four rows 4 j.. 4 j + 3 per 16 lanes: with 256-byte rows
-    // (128 dimensions) the slots must also differ above bit 0 across those rows,
-    // which the row index rotated left by one bit gives (r % 16 has the two rows'
-    // adjacent pieces collide in pairs, 2-way bank conflicts); with 128-byte rows
-    // the row parity already separates them.
+    // of row r is stored at piece slot p ^ swz(r).  The mask is chosen for the two
+    // reads of a tile: the 16-byte K-operand reads (16 rows, one piece each) and the
+    // transposing V reads (8 bytes from two adjacent pieces of four rows per 16
+    // lanes).  With 256-byte rows (128 dimensions), measured with the LDS
+    // bank-conflict counters: swz = r % 16 leaves the V reads 2-way conflicted on
+    // 40% of their cycles, a rotation of r clears them but conflicts the K reads;
+    // the mask below (bit 3 = r0 ^ r1 ^ r3, bit 2 = r1, bit 1 = r2) has no
+    // conflict in either.  128-byte rows keep r % 8.
     // Chunks arrive by direct global-to-LDS loads (no registers in between).
     __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][kKT * ROWB];
     __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][kKT * ROWB];
@@ -75,7 +76,8 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
     const int G = a.num_heads / a.num_kv_heads;
     const int bs = 1 << a.log2_bs;
     auto swz = [](int r) -> int {
-        if constexpr (PPR == 16) return ((r << 1) & 14) | ((r >> 3) & 1);
+        if constexpr (PPR == 16)
+            return (((r ^ (r >> 1) ^ (r >> 3)) & 1) << 3) | (((r >> 1) & 1) << 2) | (((r >> 2) & 1) << 1);
         return r % PPR;
     };
 
