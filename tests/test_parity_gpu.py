@@ -688,8 +688,14 @@ MFMA_CASES = [
     ("fp8_e4m3", "bf16", 128, 16, 16, 2, [7, 300]),
     ("fp8_e4m3", "f16", 128, 32, 24, 2, [31, 90]),
     ("f16", "f16", 128, 1, 4, 2, [1, 2, 45]),
-    # G > 16: one wavefront per 16-head tile, shared LDS staging
+    # G > 16: a workgroup per KV head, K/V staged once in LDS; tiles of 16 heads taken
+    # whole by one wavefront, or by four that take a quarter of every step each and
+    # merge (2 and 5 tiles); 3, 4, 6, 7, 8 tiles and a last tile with one head
     ("fp8_e4m3", "f16", 64, 16, 71, 1, [1, 2, 31, 32, 33, 700, 2048]),
+    ("fp8_e4m3", "bf16", 64, 16, 40, 1, [3, 64, 65, 500]),
+    ("bf16", "bf16", 128, 16, 90, 1, [1, 300]),
+    ("f16", "f16", 64, 8, 34, 2, [2, 130, 777]),
+    ("fp8_e4m3", "bf16", 64, 32, 80, 1, [63, 64, 65, 1200]),
     ("fp8_e4m3", "bf16", 64, 8, 71, 1, [5, 100, 513]),
     ("f16", "f16", 128, 16, 64, 2, [17, 300]),
     ("bf16", "bf16", 128, 32, 64, 1, [1, 64, 200]),
