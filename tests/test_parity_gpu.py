@@ -341,6 +341,39 @@ def test_serving_loop_many_steps():
     assert copies >= 3          # the forks from partly filled blocks were copied on write
 
 
+def test_side_stream_without_workspace():
+    """A call on a side stream with no workspace: the binding allocates the
+    partial records in that stream's order, so memory the current stream takes
+    (and overwrites) right after the call cannot be the records the kernels are
+    still using.  Balanced and partitioned modes (both write records), checked
+    against the oracle after the current stream has filled fresh allocations."""
+    case = W.make_decode_case("side_stream", "tiny", num_seqs=48, num_heads=16, num_kv_heads=2,
+                              head_dim=128, block_size=16,
+                              context_lens=np.random.default_rng(7).integers(300, 3000, 48).tolist(),
+                              kv_dtype="bf16", q_dtype="bf16", spare_blocks=5, salt=7)
+    kp, vp, ref = oracle_step(case)
+    dev = DeviceCase(case)
+    dev.write()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    say("[case] side stream, no workspace")
+    for ps in (pa.PARTITION_BALANCED, 256):
+        out = torch.full_like(dev.q, float("nan"))
+        side.wait_stream(torch.cuda.current_stream())
+        pa.paged_attention_decode(out, dev.q, dev.k_pool, dev.v_pool, dev.tables, dev.ctx,
+                                  max_context_len=case.max_context_len, scale=case.scale,
+                                  partition_size=ps, stream=side)
+        # the current stream allocates and writes straight away, while the side
+        # stream's kernels may still run
+        junk = [torch.full((1 << 20,), float("nan"), device="cuda") for _ in range(64)]
+        side.synchronize()
+        torch.cuda.synchronize()
+        del junk
+        err = max_err(out_to_f64(out), ref, case.q_dtype)
+        say(f"    partition {ps}: max-abs error {err:.3g}")
+        assert err <= TOL[case.kv_dtype], (ps, err)
+
+
 def test_two_threads_two_streams():
     """Two host threads, each with its own stream and workspace, run cache
     writes and attention on different cases at the same time (the library
