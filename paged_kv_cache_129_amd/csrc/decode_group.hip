@@ -272,12 +272,15 @@ void decode_group_kernel(DecodeArgs a) {
                     }
                 };
                 // Online-softmax update of tile ti with the scores sc[0..nv) of chunk
-                // c0 (value e is token c0 + bit(e)) into weights pr: one maximum, one
-                // check of the reference maximum (the accumulators are rescaled only
-                // when a score passes it by more than kSlack).  Unless every token is
-                // present (`fast`), absent ones are masked; the mask is built inside
-                // the masked branches only, so that none of its work reaches the
-                // common path.
+                // c0 (value e is token c0 + 4 j + bit(e)) into weights pr: one maximum,
+                // one check of the reference maximum (the accumulators are rescaled
+                // only when a score passes it by more than kSlack).  Unless every
+                // token is present (`fast`), absent ones are masked; the mask is built
+                // inside the masked branches only, so that none of its work reaches
+                // the common path, and shifted by the lane's 4 j once, so that the
+                // per-value bits are constants (with the lane's offset in each bit
+                // position, the compiler kept sixteen 64-bit masks in registers for
+                // the whole loop: 40 registers).
                 auto softmax = [&](int ti, const f32x4* sc, float* pr, int nv, bool fast, int c0,
                                    auto&& bit) {
                     float lm = kNegInfG;
@@ -285,7 +288,7 @@ void decode_group_kernel(DecodeArgs a) {
                         for (int e = 0; e < nv; ++e) lm = fmaxf(lm, sc[e >> 2][e & 3]);
                         lm *= a.qk_scale;
                     } else {
-                        const uint64_t pm = chunk_mask(c0);
+                        const uint64_t pm = chunk_mask(c0) >> (4 * j);
                         for (int e = 0; e < nv; ++e)
                             lm = fmaxf(lm, ((pm >> bit(e)) & 1ull) ? sc[e >> 2][e & 3] * a.qk_scale : kNegInfG);
                     }
@@ -302,7 +305,7 @@ void decode_group_kernel(DecodeArgs a) {
                     }
                     for (int e = 0; e < nv; ++e) pr[e] = fast_exp2(fmaf(sc[e >> 2][e & 3], a.qk_scale, -m[ti]));
                     if (!fast) {                                 // absent tokens weigh nothing
-                        const uint64_t pm = chunk_mask(c0);
+                        const uint64_t pm = chunk_mask(c0) >> (4 * j);
                         for (int e = 0; e < nv; ++e) pr[e] = ((pm >> bit(e)) & 1ull) ? pr[e] : 0.0f;
                     }
                 };
@@ -346,7 +349,7 @@ void decode_group_kernel(DecodeArgs a) {
                     }
                     float pr[4 * NQ];
                     softmax(0, sc, pr, 4 * NQ, fast, c0,
-                            [&](int e) { return 16 * (e >> 2) + 4 * j + (e & 3); });
+                            [&](int e) { return 16 * (e >> 2) + (e & 3); });
 #pragma unroll
                     for (int g = 0; g < NQ / 2; ++g) {
                         Op8 pop, plo;
@@ -386,7 +389,7 @@ void decode_group_kernel(DecodeArgs a) {
 #pragma unroll
                             for (int c = 0; c < NC; ++c) sc[0] = mma32<MT>(kop[c], qop[ti][c], sc[0]);
                             float pr[4];
-                            softmax(ti, sc, pr, 4, fast, c0, [&](int e) { return r0 + 4 * j + e; });
+                            softmax(ti, sc, pr, 4, fast, c0, [&](int e) { return r0 + e; });
                             Op4 pop, plo;
                             pack4(ti, pr, pop.w, plo.w);
 #pragma unroll
@@ -531,13 +534,17 @@ void decode_group_kernel(DecodeArgs a) {
 }
 
 // Measured on Falcon-7B's layer (71 heads of 64, fp8): 64-token steps with four
-// in flight; registers for one workgroup per CU (no spills) beat two workgroups
-// per CU with the registers capped at 128 (spilling) by 5%.
-template <int KVDT, int QDT, int D>
-hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
+// in flight.  Two workgroups per CU (four wavefronts per SIMD, at most 128
+// registers, no spills with 64 dimensions) against one (two per SIMD) on the
+// same 256-sequence fp8 MQA batch: 24 and 32 heads (one or two tiles) 31.6-32.7
+// -> 28.8-29.6 us, 48 heads 32.9-33.9 -> 31.7 us; 64, 71 and 96 heads within
+// +-1 us (the second workgroup's shorter chains are paid back by twice the cut
+// contexts and partial records), 128 heads 1 us slower.  128 dimensions do not
+// fit 128 registers.
+template <int KVDT, int QDT, int D, int MINB>
+hipError_t launch_with(DecodeArgs& a, hipStream_t stream) {
     constexpr int KT = 64;                              // tokens per step
     constexpr int NS = 4;                               // steps in flight per workgroup
-    constexpr int MINB = 1;                             // workgroups per CU the registers must allow
     auto kernel = decode_group_kernel<KVDT, QDT, D, KT, NS, MINB>;
     a.unit_heads = a.num_heads / a.num_kv_heads;        // a unit: every query head of a KV head
     a.units_per_kv = 1;
@@ -547,6 +554,14 @@ hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
     if (grid < 0) return hipErrorOutOfMemory;
     hipLaunchKernelGGL(kernel, dim3((uint32_t)grid), dim3(kGThreads), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int KVDT, int QDT, int D>
+hipError_t launch_typed(DecodeArgs& a, hipStream_t stream) {
+    const int tiles = (a.num_heads / a.num_kv_heads + 15) / 16;
+    if constexpr (D == 64)
+        if (tiles <= 3) return launch_with<KVDT, QDT, D, 2>(a, stream);
+    return launch_with<KVDT, QDT, D, 1>(a, stream);
 }
 
 template <int KVDT, int QDT>
