@@ -63,10 +63,18 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
     // 40% of their cycles, a rotation of r clears them but conflicts the K reads;
     // the mask below (bit 3 = r0 ^ r1 ^ r3, bit 2 = r1, bit 1 = r2) has no
     // conflict in either.  128-byte rows keep r % 8.
-    // Chunks arrive by direct global-to-LDS loads (no registers in between).
-    __shared__ __attribute__((aligned(1024))) uint8_t kbuf[2][kKT * ROWB];
-    __shared__ __attribute__((aligned(1024))) uint8_t vbuf[2][kKT * ROWB];
-    __shared__ __attribute__((aligned(4))) uint8_t live_s[2][kKT];
+    // Chunks arrive by direct global-to-LDS loads (no registers in between).  The two
+    // buffers are separate arrays and the chunk loop is unrolled by two, so that every
+    // LDS access names its buffer at compile time: with one array indexed by the chunk's
+    // parity, the compiler could not tell the reads of the current chunk from the loads
+    // of the next one in flight, and waited for those loads before every read (the
+    // loads then never overlapped the arithmetic).
+    __shared__ __attribute__((aligned(1024))) uint8_t kbuf0[kKT * ROWB];
+    __shared__ __attribute__((aligned(1024))) uint8_t kbuf1[kKT * ROWB];
+    __shared__ __attribute__((aligned(1024))) uint8_t vbuf0[kKT * ROWB];
+    __shared__ __attribute__((aligned(1024))) uint8_t vbuf1[kKT * ROWB];
+    __shared__ __attribute__((aligned(4))) uint8_t live0[kKT];
+    __shared__ __attribute__((aligned(4))) uint8_t live1[kKT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
         }
     };
     uint32_t absent_rows = 0;            // bit k: row of instruction k holds no token
-    auto issue_chunk = [&](int ci, int buf) {
+    auto issue_chunk = [&](int ci, uint8_t* kdst, uint8_t* vdst, uint8_t* ldst) {
         absent_rows = 0;
 #pragma unroll
         for (int k = 0; k < NLI; ++k) {
@@ -171,23 +179,23 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
                 (((int64_t)(bb * a.num_kv_heads + g) << a.log2_bs) + (live ? (t & (bs - 1)) : 0)) * ROWB +
                 lpiece[k];
             const int lbase = (wu * NLI + k) * RPI * ROWB;
-            __builtin_amdgcn_global_load_lds(kbase + off, (__attribute__((address_space(3))) void*)&kbuf[buf][lbase],
+            __builtin_amdgcn_global_load_lds(kbase + off, (__attribute__((address_space(3))) void*)&kdst[lbase],
                                              16, 0, 0);
-            __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)&vbuf[buf][lbase],
+            __builtin_amdgcn_global_load_lds(vbase + off, (__attribute__((address_space(3))) void*)&vdst[lbase],
                                              16, 0, 0);
             absent_rows |= live ? 0u : (1u << k);
-            if (lslot == 0) live_s[buf][lrow[k]] = live ? 1 : 0;
+            if (lslot == 0) ldst[lrow[k]] = live ? 1 : 0;
         }
     };
     // after this wavefront's loads of a chunk have landed: zero the V rows that hold
     // no token (their weights are zero, and 0 * NaN would poison the sums)
-    auto settle_chunk = [&](int buf) {
+    auto settle_chunk = [&](uint8_t* vcur) {
         __builtin_amdgcn_s_waitcnt(0);           // vmcnt(0): the direct loads are in LDS
         if (absent_rows) {
 #pragma unroll
             for (int k = 0; k < NLI; ++k)
                 if (absent_rows & (1u << k))
-                    *reinterpret_cast<uint4*>(&vbuf[buf][(wu * NLI + k) * RPI * ROWB + lane * 16]) =
+                    *reinterpret_cast<uint4*>(&vcur[(wu * NLI + k) * RPI * ROWB + lane * 16]) =
                         make_uint4(0u, 0u, 0u, 0u);
         }
     };
@@ -204,24 +212,24 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
 
     if (nchunks > 0) {
         load_table(0);
-        issue_chunk(0, 0);
+        issue_chunk(0, kbuf0, vbuf0, live0);
         if (nchunks > 1) load_table(1);
     }
-    for (int ci = 0; ci < nchunks; ++ci) {
-        const int buf = ci & 1;
-        settle_chunk(buf);
+    // one chunk: kt/vt/lt hold it, kn/vn/ln receive the next
+    auto chunk = [&](int ci, const uint8_t* kt, uint8_t* vt, const uint8_t* lt, uint8_t* kn, uint8_t* vn,
+                     uint8_t* ln) {
+        settle_chunk(vt);
         __syncthreads();
         if (ci + 1 < nchunks) {
-            issue_chunk(ci + 1, buf ^ 1);
+            issue_chunk(ci + 1, kn, vn, ln);
             if (ci + 2 < nchunks) load_table(ci + 2);
         }
         const int t0 = ci * kKT;
-        const uint8_t* kt = kbuf[buf];
-        const uint8_t* vt = vbuf[buf];
-        // Two 32-token steps per chunk.  The score MFMAs of both are issued first, so
-        // that the matrix cores work on the second step's scores while the vector
-        // units run the first step's softmax, and on the first step's output MFMAs
-        // while they run the second's.
+        // Two 32-token steps per chunk, one after the other.  (Issuing the score MFMAs of
+        // both first, so that the matrix cores work on the second step's scores while
+        // the vector units run the first step's softmax, needs more than 256 registers
+        // once the loop holds two buffers' addresses; the spill reloads then wait for
+        // every load in flight.)
         const bool on0 = t0 <= p_wave_max, on1 = t0 + 32 <= p_wave_max;   // scalar
         f32x4 scs[2][TQ][2];
         uint32_t lvs[2][2];
@@ -230,7 +238,7 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
             auto& sc = scs[sub];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                lv4[h] = *reinterpret_cast<const uint32_t*>(&live_s[buf][32 * sub + 16 * h + 4 * j]);
+                lv4[h] = *reinterpret_cast<const uint32_t*>(&lt[32 * sub + 16 * h + 4 * j]);
             // scores of every tile first, so that no softmax waits on its own MFMAs; each
             // K operand is read just before the MFMAs that use it (few registers live)
 #pragma unroll
@@ -367,13 +375,15 @@ __global__ __launch_bounds__(NW * 64, WPE) void prefill_mfma_kernel(PrefillArgs 
                 }
             }
         };
-        if (on0) scores(0);
-        if (on1) scores(1);
-        if (on0) step(0);
-        if (on1) step(1);
+        if (on0) { scores(0); step(0); }
+        if (on1) { scores(1); step(1); }
         // no barrier here: the next chunk goes into the other buffer, and the
         // barrier after that store orders this chunk's reads before the buffer
         // is written again
+    };
+    for (int ci = 0; ci < nchunks; ci += 2) {
+        chunk(ci, kbuf0, vbuf0, live0, kbuf1, vbuf1, live1);
+        if (ci + 1 < nchunks) chunk(ci + 1, kbuf1, vbuf1, live1, kbuf0, vbuf0, live0);
     }
 
     // ---- normalise and store: lane holds column c16 of each tile, d = 16 dt + 4 j .. + 3
