@@ -74,6 +74,20 @@ def test_falcon7b_mqa_fp8(bs):
     run_and_check(case, partitions=(512, 0, -1))
 
 
+@pytest.mark.parametrize("H", [24, 48])
+def test_mqa_fp8_two_workgroups_per_cu(H):
+    """64-dimension groups of up to 48 heads run two workgroups per CU: twice the
+    workers of the one-workgroup launch, so twice the cut contexts and partial
+    records; the Falcon-7B batch (256 sequences of 1..2048 tokens) with 24 heads (two
+    16-head tiles, split by quarters) and 48 heads (three whole tiles)."""
+    ctx = W.falcon7b_lengths(256)
+    case = W.make_decode_case(f"mqa{H}_fp8", "falcon7b", num_seqs=256, num_heads=H,
+                              num_kv_heads=1, head_dim=64, block_size=16, context_lens=ctx,
+                              kv_dtype="fp8_e4m3", q_dtype="f16",
+                              num_blocks=W.falcon7b_num_blocks(ctx, 16), salt=H)
+    run_and_check(case, partitions=(-1, 512))
+
+
 def _llama70b(spec, num_blocks):
     order = W.free_order("llama70b", num_blocks)
     lib_alloc = pa.BlockAllocator(num_blocks, 16, order)
