@@ -102,6 +102,19 @@ def test_small_mixes(idx):
     check(case)
 
 
+@pytest.mark.parametrize("kv,scale", [("f16", 1.0), ("f16", -0.088), ("bf16", -0.088)])
+def test_scales(kv, scale):
+    """Softmax scales other than 1/sqrt(D): a scale of 1 (1.44 in log2 units) and a
+    negative one, which flips every score's sign (the kernel's mask-free path takes
+    the largest scaled score from the largest score only for positive scales)."""
+    import dataclasses
+    case = W.make_prefill_case(f"scale_{kv}_{scale}", "tiny", prior_lens=[0, 90, 300],
+                               chunk_lens=[70, 33, 129], num_heads=8, num_kv_heads=2,
+                               head_dim=128, block_size=16, kv_dtype=kv, q_dtype=kv,
+                               spare_blocks=3, value_scale=0.3, salt=77)
+    check(dataclasses.replace(case, scale=scale), label=f"scale {scale}")
+
+
 @pytest.mark.parametrize("seed", range(12))
 def test_random_mixes(seed):
     r = np.random.default_rng(1000 + seed)
