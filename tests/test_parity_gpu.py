@@ -996,6 +996,28 @@ def _random_config(seed):
     return kv, q, D, bs, G * Hkv, Hkv, [int(c) for c in ctx]
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_large_groups_many_sequences(seed):
+    """The workgroup kernel (17-128 query heads per KV head) over batches of 100-600
+    sequences: many workers, contexts cut across workers at every range boundary,
+    items of every length, one or two workgroups per CU by head count."""
+    r = np.random.default_rng(7000 + seed)
+    kv, q = [("fp8_e4m3", "f16"), ("fp8_e4m3", "bf16"), ("f16", "f16"), ("bf16", "bf16")][seed % 4]
+    D = [64, 128][(seed // 2) % 2] if kv != "fp8_e4m3" or seed % 3 else 64
+    G = int(r.choice([17, 24, 40, 48, 64, 71, 100, 128]))
+    Hkv = int(r.choice([1, 2]))
+    bs = int(r.choice([8, 16, 32, 64]))
+    S = int(r.integers(100, 600))
+    ctx = (r.integers(1, 1500, size=S) if seed % 2 else
+           np.clip(np.rint(np.exp(r.normal(np.log(300), 0.9, size=S))), 1, 3000)).astype(int)
+    say(f"[case] large groups seed {seed}: {kv}/{q} D={D} G={G} Hkv={Hkv} bs={bs} S={S}")
+    case = W.make_decode_case(f"large_group_{seed}", "tiny", num_seqs=S, num_heads=G * Hkv,
+                              num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                              context_lens=[int(c) for c in ctx], kv_dtype=kv, q_dtype=q,
+                              spare_blocks=9, salt=300 + seed)
+    run_and_check(case, partitions=(-1, 512))
+
+
 @pytest.mark.parametrize("seed", range(48))
 def test_random_configurations(seed):
     kv, q, D, bs, H, Hkv, ctx = _random_config(seed)
