@@ -1018,6 +1018,29 @@ def test_random_large_groups_many_sequences(seed):
     run_and_check(case, partitions=(-1, 512))
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_random_small_groups_many_sequences(seed):
+    """The per-head (G = 1) and per-tile (2-16 heads per KV head) kernels over batches
+    of 100-600 sequences: many workers (one per wavefront), every range boundary
+    cutting a context."""
+    r = np.random.default_rng(8000 + seed)
+    kv, q = [("f16", "f16"), ("bf16", "bf16"), ("fp8_e4m3", "f16"), ("f32", "f32"),
+             ("fp8_e4m3", "bf16"), ("f16", "f16")][seed]
+    D = [64, 128][seed % 2]
+    G = int(r.choice([1, 2, 4, 8, 16]))
+    Hkv = int(r.choice([1, 2, 4, 8]))
+    bs = int(r.choice([8, 16, 32]))
+    S = int(r.integers(100, 600))
+    ctx = (r.integers(1, 1200, size=S) if seed % 2 else
+           np.clip(np.rint(np.exp(r.normal(np.log(250), 0.9, size=S))), 1, 2500)).astype(int)
+    say(f"[case] small groups seed {seed}: {kv}/{q} D={D} G={G} Hkv={Hkv} bs={bs} S={S}")
+    case = W.make_decode_case(f"small_group_{seed}", "tiny", num_seqs=S, num_heads=G * Hkv,
+                              num_kv_heads=Hkv, head_dim=D, block_size=bs,
+                              context_lens=[int(c) for c in ctx], kv_dtype=kv, q_dtype=q,
+                              spare_blocks=9, salt=400 + seed)
+    run_and_check(case, partitions=(-1, 512))
+
+
 @pytest.mark.parametrize("seed", range(48))
 def test_random_configurations(seed):
     kv, q, D, bs, H, Hkv, ctx = _random_config(seed)
