@@ -497,6 +497,70 @@ def test_llama7b_full_size_sampled():
     del d
 
 
+def test_llama7b_full_step_every_sequence_layer():
+    """The whole Llama-2-7B decode step in its timed launch configuration: 32 layers,
+    each with its own 17,408-block pools (4.25 GiB of K+V per layer, one block table
+    for all layers), 64 sequences at context 4096, per layer the cache write and then
+    single-pass attention with a caller workspace.  Every one of the 2,048
+    sequence-layers is recomputed by the oracle from its blocks as the step left them
+    (the oracle rewrites the new token's slot, whose bytes must already be the GPU's)."""
+    import concurrent.futures as cf
+    S, H, Hkv, D, bs, NB, L = 64, 32, 32, 128, 16, 17408, 32
+    nblk = 4096 // bs
+    ctx = np.full(S, 4096, dtype=np.int32)
+    say(f"[case] llama7b full step: {L} layers of 4.25 GiB pools on device")
+    layers = [W.device_pool_case(f"llama7b_l{l}", "llama7b", num_seqs=S, num_heads=H,
+                                 num_kv_heads=Hkv, head_dim=D, block_size=bs, context_lens=ctx,
+                                 kv_dtype="f16", num_blocks=NB, layer=l, place_layer=0)
+              for l in range(L)]
+    tab = layers[0]["tables"]
+    tables = torch.from_numpy(tab).cuda()
+    ctx_t = torch.from_numpy(ctx).cuda()
+    slots = torch.from_numpy(layers[0]["slots"]).cuda()
+    ws = pa.new_workspace(pa.paged_attention_workspace_size(S, H, Hkv, D, 4096, 0), "cuda")
+    for d in layers:
+        d["out"] = torch.full_like(d["q"], float("nan"))
+        pa.kv_cache_write(d["k_new"], d["v_new"], d["k_pool"], d["v_pool"], slots)
+        pa.paged_attention_decode(d["out"], d["q"], d["k_pool"], d["v_pool"], tables, ctx_t,
+                                  max_context_len=4096, scale=d["scale"], partition_size=0,
+                                  workspace=ws)
+    torch.cuda.synchronize()
+    scale = layers[0]["scale"]
+    host = [dict(q=d["q"].cpu().numpy(), kn=d["k_new"].cpu().numpy(), vn=d["v_new"].cpu().numpy(),
+                 out=out_to_f64(d["out"])) for d in layers]
+    local = np.arange(nblk, dtype=np.int32)[None, :]
+    slot = np.array([(nblk - 1) * bs + (4095 % bs)])
+
+    def check(x):
+        l, s, kp, vp = x
+        h = host[l]
+        got_k, got_v = kp[nblk - 1, :, 4095 % bs, :].copy(), vp[nblk - 1, :, 4095 % bs, :].copy()
+        oracle.kv_write(kp, vp, "f16", h["kn"][s:s + 1], h["vn"][s:s + 1], "f16", slot, bs)
+        same = (np.array_equal(got_k.view(np.uint16), kp[nblk - 1, :, 4095 % bs, :].view(np.uint16)) and
+                np.array_equal(got_v.view(np.uint16), vp[nblk - 1, :, 4095 % bs, :].view(np.uint16)))
+        ref = oracle.paged_attention(h["q"][s:s + 1], "f16", kp, vp, "f16", local, [4096], bs, scale)[0]
+        return l, s, same, bool(np.isfinite(h["out"][s]).all()), max_err(h["out"][s], ref, "f16")
+
+    work = [(l, s) for l in range(L) for s in range(S)]
+    results = []
+    with cf.ThreadPoolExecutor(16) as ex:
+        for i in range(0, len(work), 16):
+            xs = []
+            for l, s in work[i:i + 16]:
+                idx = torch.from_numpy(tab[s, :nblk].astype(np.int64)).cuda()
+                xs.append((l, s, layers[l]["k_pool"][idx].cpu().numpy(),
+                           layers[l]["v_pool"][idx].cpu().numpy()))
+            results += list(ex.map(check, xs))
+    worst = max(results, key=lambda r: r[4])
+    say(f"    {len(results)} sequence-layers: worst max-abs error {worst[4]:.3g} "
+        f"(layer {worst[0]}, sequence {worst[1]})")
+    assert all(r[2] for r in results), "a written slot differs from the oracle's encoding"
+    assert all(r[3] for r in results)
+    assert worst[4] <= TOL["f16"]
+    del layers, ws
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------------ edge cases
 EDGE = [
     # kv, q, D, bs, H, Hkv, ctx
