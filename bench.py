@@ -689,6 +689,29 @@ def allocator_study(pa):
 
 
 # ---------------------------------------------------------------- main
+def reference_read_gbs(torch, pa, mib=2048, reps=10):
+    """The library's streaming-read probe over `mib` MiB (the decode kernels' 16-byte
+    non-temporal loads, nothing else): the read rate this device reaches, beside the
+    8 TB/s denominator.  Measured before the workload's pools are allocated."""
+    n = mib << 20
+    buf = torch.ones(n // 4, dtype=torch.int32, device="cuda")
+    sink = torch.zeros(pa.STREAM_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    pa.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    gbs = 0.0
+    for _ in range(3):          # the best of three timings: a ceiling, not an average
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            pa.stream_read(buf, sink)
+        b.record()
+        torch.cuda.synchronize()
+        gbs = max(gbs, float(n) * reps / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf, sink
+    torch.cuda.empty_cache()
+    return gbs
+
+
 def reference_copy_gbs(torch, mib=512, reps=10):
     """Device-to-device copy of `mib` MiB with the runtime's copy (read + write bytes
     per second): the bandwidth a plain streaming kernel reaches on this device,
@@ -834,7 +857,9 @@ def main():
     if args.calibrate_copy_mib > 0:
         calibrate_copy(pa, torch, args.calibrate_copy_mib)
     copy_gbs = reference_copy_gbs(torch)
-    log(f"reference device-to-device copy: {copy_gbs:.0f} GB/s (read + write)")
+    read_gbs = reference_read_gbs(torch, pa)
+    log(f"reference device-to-device copy: {copy_gbs:.0f} GB/s (read + write); "
+        f"streaming read: {read_gbs:.0f} GB/s")
     if args.partition_size is None:
         args.partition_size = DEFAULT_PARTITION[args.workload]
     wl = WORKLOADS[args.workload](pa, W, torch, args.partition_size, args)
@@ -869,7 +894,8 @@ def main():
                      "avg_launch_us": round(decode_ms * 1e3, 2),
                      "single_call_us_p10_p50_p90": spread,
                      "traffic_source": traffic_src,
-                     "reference_copy_gbs": round(copy_gbs, 1)},
+                     "reference_copy_gbs": round(copy_gbs, 1),
+                     "reference_read_gbs": round(read_gbs, 1)},
         "cpu_baseline": None,
     }
     import oracle

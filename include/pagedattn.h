@@ -356,6 +356,25 @@ pa_status pa_swap_blocks(void* const* dst_pools, const void* const* src_pools, i
                          int64_t block_bytes, int32_t dst_num_blocks, int32_t src_num_blocks,
                          const int32_t* pairs, int32_t num_pairs, void* stream);
 
+/*
+ * stream_read — a measurement aid, not part of the attention path: reads
+ * `bytes` bytes of device memory once with the same 16-byte streaming
+ * (non-temporal) loads, consecutive lanes on consecutive pieces, that the
+ * decode kernels use for K and V, so that the rate their HBM rooflines are
+ * compared with can be measured on the device at hand (time it with events on
+ * `stream`).
+ *
+ *   buf    DEVICE memory, 16-byte aligned; bytes: a positive multiple of 16
+ *   sink   DEVICE uint32 [PA_STREAM_READ_SINK_WORDS], caller-owned; the call
+ *          writes the XOR of all of buf's 32-bit words, folded per workgroup,
+ *          into its first words (the XOR of every sink word written equals the
+ *          XOR of buf's words when the sink was zeroed first)
+ *   stream hipStream_t (NULL: the default stream)
+ * Errors: PA_ERR_INVALID_ARG for a null, misaligned or badly sized argument.
+ */
+#define PA_STREAM_READ_SINK_WORDS 4096
+pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* ------------------------------------------------------------------------
  * Host block allocator: free list, per-block reference counts, block tables
  * and copy-on-write (KV 缓存与分页注意力 §07 块表, §08 共用，写时复制;

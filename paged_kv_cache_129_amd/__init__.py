@@ -65,6 +65,7 @@ _SIGNATURES = [
     ("pa_copy_blocks", ctypes.c_int32,
      [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
       ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
+    ("pa_stream_read", ctypes.c_int32, [_vp, ctypes.c_size_t, _vp, _vp]),
     ("pa_swap_blocks", ctypes.c_int32,
      [ctypes.POINTER(_vp), ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64, ctypes.c_int32,
       ctypes.c_int32, _vp, ctypes.c_int32, _vp]),
@@ -462,6 +463,27 @@ def swap_blocks(dst_pools: Sequence, src_pools: Sequence, pairs, *, stream=None)
     _check(lib.pa_swap_blocks(dp, sp, L, block_bytes, dst_pools[0].shape[0], src_pools[0].shape[0],
                               _dev(dpairs, "pairs"), dpairs.shape[0], ctypes.c_void_p(s.cuda_stream)),
            "swap_blocks")
+
+
+STREAM_READ_SINK_WORDS = 4096
+
+
+def stream_read(buf, sink, *, stream=None) -> None:
+    """One pass of the decode kernels' 16-byte streaming loads over the contiguous
+    device tensor ``buf`` (a multiple of 16 bytes); ``sink`` is a device int32 or
+    uint32 tensor of STREAM_READ_SINK_WORDS words that receives the XOR of buf's
+    32-bit words, folded per workgroup.  A measurement aid: the read rate the HBM
+    rooflines are compared with."""
+    torch = _torch()
+    if not buf.is_contiguous() or not sink.is_contiguous():
+        raise ValueError("buf and sink must be contiguous")
+    if sink.numel() * sink.element_size() < 4 * STREAM_READ_SINK_WORDS:
+        raise ValueError(f"sink must hold {STREAM_READ_SINK_WORDS} 32-bit words")
+    _one_device(buf, sink)
+    nbytes = buf.numel() * buf.element_size()
+    s = stream if stream is not None else torch.cuda.current_stream(buf.device)
+    _check(lib.pa_stream_read(_dev(buf, "buf"), nbytes, _dev(sink, "sink"),
+                              ctypes.c_void_p(s.cuda_stream)), "stream_read")
 
 
 # ------------------------------------------------------------------ host allocator

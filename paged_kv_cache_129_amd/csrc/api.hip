@@ -522,4 +522,13 @@ pa_status pa_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num
     return PA_OK;
 }
 
+pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink || !aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) || bytes == 0 ||
+        bytes % 16 != 0 || bytes > (size_t)INT64_MAX)
+        return PA_ERR_INVALID_ARG;
+    return launch_checked([&] {
+        return pa::launch_stream_read(buf, (int64_t)bytes, sink, as_stream(stream));
+    });
+}
+
 }  // extern "C"

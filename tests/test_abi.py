@@ -211,3 +211,13 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(ValueError, match="device tensor"):
         pa.paged_attention_decode(torch.empty_like(q), q, kp, vp, tables, ctx,
                                   max_context_len=64, scale=0.125)
+
+
+def test_stream_read_rejects_bad_arguments():
+    # each of these fails validation before anything reaches the device
+    assert lib.pa_stream_read(NULL, 16, FAKE, NULL) == -1
+    assert lib.pa_stream_read(FAKE, 16, NULL, NULL) == -1
+    assert lib.pa_stream_read(FAKE, 0, FAKE, NULL) == -1
+    assert lib.pa_stream_read(FAKE, 24, FAKE, NULL) == -1
+    assert lib.pa_stream_read(ctypes.c_void_p(0x1008), 16, FAKE, NULL) == -1
+    assert lib.pa_stream_read(FAKE, 16, ctypes.c_void_p(0x1002), NULL) == -1

@@ -561,6 +561,22 @@ def test_llama7b_full_step_every_sequence_layer():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("nbytes", [16, 16 * 1000 + 16, 64 << 20])
+def test_stream_read_reads_every_word(nbytes):
+    """The read-rate probe visits every 16-byte piece once: the XOR of its sink words
+    equals the XOR of the buffer's words."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(nbytes)
+    buf = torch.randint(-2**31, 2**31 - 1, (nbytes // 4,), dtype=torch.int32, device="cuda",
+                        generator=g)
+    sink = torch.zeros(pa.STREAM_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    pa.stream_read(buf, sink)
+    torch.cuda.synchronize()
+    want = np.bitwise_xor.reduce(buf.cpu().numpy().view(np.uint32))
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == want
+
+
 # ------------------------------------------------------------------ edge cases
 EDGE = [
     # kv, q, D, bs, H, Hkv, ctx
