@@ -343,6 +343,11 @@ pa_status decode_impl(void* out, const void* q, int32_t q_dtype,
 
 }  // namespace
 
+namespace pa {
+// the streaming-read probe's launcher (copy_blocks.hip); not part of the decode path
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+}  // namespace pa
+
 extern "C" {
 
 pa_status pa_paged_attention_decode(void* out, const void* q, int32_t q_dtype,

@@ -114,7 +114,7 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hi
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         cus = 256;
     const int64_t grid = std::min<int64_t>({(int64_t)cus, (pieces + kThreads - 1) / kThreads,
-                                            (int64_t)kStreamReadSinkWords});
+                                            (int64_t)PA_STREAM_READ_SINK_WORDS});
     hipLaunchKernelGGL(stream_read_kernel, dim3((uint32_t)grid), dim3(kThreads), 0, stream,
                        reinterpret_cast<const char*>(buf), pieces, sink);
     return hipGetLastError();

@@ -5,8 +5,6 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "pagedattn.h"
-
 namespace pa {
 
 struct WriteArgs {
@@ -52,11 +50,6 @@ struct SwapArgs {
     int32_t slices;                     // set at launch
 };
 hipError_t launch_swap_blocks(SwapArgs& a, hipStream_t stream);
-
-// one pass of streaming 16-byte loads over `bytes` bytes (a multiple of 16);
-// sink receives one word per workgroup (at most kStreamReadSinkWords)
-constexpr int kStreamReadSinkWords = PA_STREAM_READ_SINK_WORDS;
-hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
 
 // Sequences are scheduled in windows of kWindow (their metadata is staged in
 // LDS).  The balanced schedule gives each worker (a wavefront) two

@@ -117,3 +117,19 @@ def test_paged_policy_readout_matches_the_oracle_model():
         lib = bench.serve_trace(bench.Paged(pa, 176, bs), [1] * 30, finals)
         mod = bench.serve_trace(ModelPaged(176, bs), [1] * 30, finals)
         assert lib == mod
+
+
+def test_committed_traffic_figures_match_the_sources():
+    """Every committed counter summary still describes the kernels as they are: its
+    sources hash to the recorded value, so bench.py reports its figure."""
+    import glob
+    paths = sorted(glob.glob(os.path.join(bench.ROOT, "profiles", "*.traffic.txt")))
+    assert paths
+    for path in paths:
+        kv = dict(line.split("=", 1) for line in open(path)
+                  if "=" in line and not line.lstrip().startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        figure, name = bench.read_traffic(kv["workload"], int(kv["partition_size"]),
+                                          int(kv.get("block_size", "0")))
+        assert name == os.path.basename(path), path
+        assert figure == int(float(kv["traffic_bytes"]))
