@@ -60,9 +60,10 @@ __global__ __launch_bounds__(kThreads) void swap_blocks_kernel(SwapArgs a) {
 // per CU, each on a contiguous span, each thread with kReadRing loads in
 // flight, and folds every word into one XOR per workgroup so the loads cannot
 // be dropped.  It measures the read rate those kernels' HBM rooflines are set
-// against on the device at hand.  Measured over 2 GiB: one workgroup of 256
-// threads per CU with eight loads per thread reached 7.0-7.2 TB/s; four loads,
-// or two to eight workgroups per CU, 5.5-7.0 TB/s.
+// against on the device at hand.  Measured over 2 GiB, one workgroup of 256
+// threads per CU with eight loads per thread was the fastest launch shape
+// (7.2 TB/s on one device, 6.5-6.7 TB/s on another); four loads per thread,
+// more workgroups per CU, 512 or 1,024 threads or a grid stride were not faster.
 constexpr int kReadRing = 8;
 
 __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* buf, int64_t pieces,
@@ -71,9 +72,9 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* buf, 
     const int64_t base = min(pieces, (int64_t)blockIdx.x * per);
     const int64_t p1 = min(pieces, base + per);             // this workgroup's span ends here
     const int64_t p0 = base + threadIdx.x;                  // the thread's first piece
-    // loads past the span read the buffer's last piece again (in bounds) and are not folded
-    // (the same non-temporal 16-byte load as load16_stream, kept as a vector so that
-    // the folds wait for each load in turn rather than for all eight)
+    // the same non-temporal 16-byte load as load16_stream, kept as a vector so that
+    // the folds wait for each load in turn rather than for all eight; loads past the
+    // span read the buffer's last piece again (in bounds) and are not folded
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
     auto ld = [&](int64_t i) {
         return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(buf + min(i, pieces - 1) * 16));
