@@ -370,7 +370,9 @@ pa_status pa_swap_blocks(void* const* dst_pools, const void* const* src_pools, i
  *          into its first words (the XOR of every sink word written equals the
  *          XOR of buf's words when the sink was zeroed first)
  *   stream hipStream_t (NULL: the default stream)
- * Errors: PA_ERR_INVALID_ARG for a null, misaligned or badly sized argument.
+ * Errors: PA_ERR_INVALID_ARG for a null, misaligned or badly sized argument, or
+ * when [buf, buf + bytes) or the sink does not lie inside one HIP allocation
+ * (checked with hipMemGetAddressRange before anything is enqueued).
  */
 #define PA_STREAM_READ_SINK_WORDS 4096
 pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);

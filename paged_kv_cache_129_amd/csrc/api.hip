@@ -527,9 +527,24 @@ pa_status pa_copy_blocks(void* const* k_pools, void* const* v_pools, int32_t num
     return PA_OK;
 }
 
+// whether [p, p + bytes) lies inside one allocation HIP knows
+static bool inside_allocation(const void* p, size_t bytes) {
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, const_cast<void*>(p)) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base), q = reinterpret_cast<uintptr_t>(p);
+    return q >= b && bytes <= size && q - b <= size - bytes;
+}
+
 pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
     if (!buf || !sink || !aligned16(buf) || (reinterpret_cast<uintptr_t>(sink) & 3u) || bytes == 0 ||
         bytes % 16 != 0 || bytes > (size_t)INT64_MAX)
+        return PA_ERR_INVALID_ARG;
+    if (!inside_allocation(buf, bytes) ||
+        !inside_allocation(sink, sizeof(uint32_t) * PA_STREAM_READ_SINK_WORDS))
         return PA_ERR_INVALID_ARG;
     return launch_checked([&] {
         return pa::launch_stream_read(buf, (int64_t)bytes, sink, as_stream(stream));

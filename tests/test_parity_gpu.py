@@ -577,6 +577,23 @@ def test_stream_read_reads_every_word(nbytes):
     assert got == want
 
 
+def test_stream_read_refuses_ranges_past_the_allocation():
+    """A range longer than any allocation, and memory HIP does not know, are refused on
+    the host (nothing is enqueued).  (torch's caching allocator carves tensors out of
+    larger segments, so a range just past a tensor's end may still lie inside one.)"""
+    import ctypes
+    buf = torch.empty(64 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(pa.STREAM_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    read = pa.lib.pa_stream_read
+    assert read(ctypes.c_void_p(buf.data_ptr()), 64 << 20, ctypes.c_void_p(sink.data_ptr()), s) == 0
+    assert read(ctypes.c_void_p(buf.data_ptr()), 1 << 40, ctypes.c_void_p(sink.data_ptr()), s) == -1
+    host = np.zeros(1 << 16, dtype=np.uint8)
+    assert read(ctypes.c_void_p(host.ctypes.data), 16, ctypes.c_void_p(sink.data_ptr()), s) == -1
+    assert read(ctypes.c_void_p(buf.data_ptr()), 16, ctypes.c_void_p(host.ctypes.data), s) == -1
+    torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ edge cases
 EDGE = [
     # kv, q, D, bs, H, Hkv, ctx
